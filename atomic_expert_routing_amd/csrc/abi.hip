@@ -1,0 +1,188 @@
+// C ABI of libomni.so: host-side validation, workspace carving and launches.
+// Every check runs before the first launch, so a rejected call enqueues
+// nothing and leaves every output untouched.
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "omni_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+omni_status fail(omni_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+omni_status ok() {
+  g_err[0] = '\0';
+  return OMNI_OK;
+}
+
+omni_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(OMNI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t I32_LIMIT = 2147483647;
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+omni_status check_dtype_d(omni_dtype dt, int64_t d) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return fail(OMNI_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (d <= 0) return fail(OMNI_ERR_INVALID_ARG, "d must be positive (got %lld)", (long long)d);
+  if (d % 8) return fail(OMNI_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  const int64_t dmax = dt == OMNI_BF16 ? OMNI_MAX_D_BF16 : OMNI_MAX_D_F32;
+  if (d > dmax) return fail(OMNI_ERR_UNSUPPORTED, "d = %lld exceeds %lld", (long long)d, (long long)dmax);
+  return OMNI_OK;
+}
+
+omni_status check_tasks(int64_t L, int64_t K) {
+  if (L <= 0 || K <= 0)
+    return fail(OMNI_ERR_INVALID_ARG, "L and K must be positive (L=%lld K=%lld)", (long long)L, (long long)K);
+  if (L > I32_LIMIT / K)
+    return fail(OMNI_ERR_UNSUPPORTED, "L*K = %lld tasks exceeds 2^31-1", (long long)(L * K));
+  return OMNI_OK;
+}
+
+omni_status router_ws(int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = check_dtype_d(dt, d)) != OMNI_OK) return s;
+  if ((s = check_tasks(L, K)) != OMNI_OK) return s;
+  if (Nr <= 0 || Nc <= 0)
+    return fail(OMNI_ERR_INVALID_ARG, "N_r and N_c must be positive (%lld, %lld)", (long long)Nr, (long long)Nc);
+  if (Nr > OMNI_MAX_GRID_SIDE || Nc > OMNI_MAX_GRID_SIDE)
+    return fail(OMNI_ERR_UNSUPPORTED, "grid side above %d (N_r=%lld N_c=%lld)", OMNI_MAX_GRID_SIDE,
+                (long long)Nr, (long long)Nc);
+  if (K > Nr * Nc)
+    return fail(OMNI_ERR_INVALID_ARG, "K = %lld exceeds N_r*N_c = %lld", (long long)K, (long long)(Nr * Nc));
+  if (K > OMNI_MAX_K) return fail(OMNI_ERR_UNSUPPORTED, "K = %lld exceeds %d", (long long)K, OMNI_MAX_K);
+  if (L > I32_LIMIT / (Nr + Nc)) return fail(OMNI_ERR_UNSUPPORTED, "L*(N_r+N_c) exceeds 2^31-1");
+  *out = align256((size_t)L * (size_t)(Nr + Nc) * 4);
+  return OMNI_OK;
+}
+
+omni_status schedule_ws(int64_t L, int64_t K, int64_t N, int64_t B, size_t* out) {
+  omni_status s;
+  if ((s = check_tasks(L, K)) != OMNI_OK) return s;
+  if (N <= 0 || B <= 0)
+    return fail(OMNI_ERR_INVALID_ARG, "N and B must be positive (N=%lld B=%lld)", (long long)N, (long long)B);
+  if (N > I32_LIMIT) return fail(OMNI_ERR_UNSUPPORTED, "N = %lld exceeds 2^31-1", (long long)N);
+  *out = omni::plan_schedule(L, K, N, B).ws_bytes;
+  return OMNI_OK;
+}
+
+omni_status expert_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = check_dtype_d(dt, d)) != OMNI_OK) return s;
+  if ((s = check_tasks(L, K)) != OMNI_OK) return s;
+  if (N <= 0) return fail(OMNI_ERR_INVALID_ARG, "N must be positive (got %lld)", (long long)N);
+  if (N > I32_LIMIT) return fail(OMNI_ERR_UNSUPPORTED, "N = %lld exceeds 2^31-1", (long long)N);
+  *out = align256((size_t)L * (size_t)K * 4);
+  return OMNI_OK;
+}
+
+omni_status check_ws(const void* ws, size_t have, size_t need) {
+  if (have < need)
+    return fail(OMNI_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
+  if (need && !ws) return fail(OMNI_ERR_INVALID_ARG, "workspace pointer is NULL");
+  if ((uintptr_t)ws % 256) return fail(OMNI_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return OMNI_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+omni_status omni_router(const void* x, const void* Wr, const void* Wc, int64_t L, int64_t d,
+                        int64_t Nr, int64_t Nc, int64_t K, omni_dtype dt, int32_t* idx,
+                        float* score, float* gate, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = router_ws(L, d, Nr, Nc, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !Wr || !Wc || !idx || !score || !gate)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_router: NULL array pointer");
+  if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wc))
+    return fail(OMNI_ERR_INVALID_ARG, "omni_router: x, Wr and Wc must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  float* logits = (float*)ws;
+  hipError_t e = omni::launch_router_gemm(x, Wr, Wc, (int)L, (int)d, (int)Nr, (int)Nc, dt, logits, st);
+  if (e != hipSuccess) return hip_status(e, "router projection launch");
+  e = omni::launch_router_topk(logits, (int)L, (int)Nr, (int)Nc, (int)K, idx, score, gate, st);
+  return hip_status(e, "router top-K launch");
+}
+
+omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K, int64_t N, int64_t B,
+                          int32_t* perm, int32_t* group_off, void* ws, size_t ws_bytes,
+                          void* stream) {
+  size_t need = 0;
+  omni_status s = schedule_ws(L, K, N, B, &need);
+  if (s != OMNI_OK) return s;
+  if (!idx || !perm || !group_off) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL array pointer");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::SchedPlan plan = omni::plan_schedule(L, K, N, B);
+  hipError_t e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws,
+                                       (hipStream_t)stream);
+  return hip_status(e, "schedule launch");
+}
+
+omni_status omni_expert_forward(const void* x, const void* W, const void* V, const int32_t* idx,
+                                const float* gate, const int32_t* perm, int64_t L, int64_t d,
+                                int64_t N, int64_t K, omni_dtype dt, float* y, void* ws,
+                                size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = expert_ws(L, d, N, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !perm || !y)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(y))
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: x, W, V and y must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  float* act = (float*)ws;
+  hipError_t e = omni::launch_expert_act(x, W, idx, gate, perm, (int)L, (int)d, (int)K, dt, act, st);
+  if (e != hipSuccess) return hip_status(e, "expert activation launch");
+  e = omni::launch_expert_out(V, idx, act, (int)L, (int)d, (int)K, dt, y, st);
+  return hip_status(e, "expert output launch");
+}
+
+omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
+                                 int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
+  if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");
+  size_t need = 0;
+  omni_status s;
+  switch (op) {
+    case OMNI_OP_ROUTER: s = router_ws(L, d, Nr, Nc, K, dt, &need); break;
+    case OMNI_OP_SCHEDULE: s = schedule_ws(L, K, N, B, &need); break;
+    case OMNI_OP_EXPERT_FORWARD: s = expert_ws(L, d, N, K, dt, &need); break;
+    default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  }
+  if (s != OMNI_OK) return s;
+  *out = need;
+  return ok();
+}
+
+const char* omni_status_string(omni_status s) {
+  switch (s) {
+    case OMNI_OK: return "ok";
+    case OMNI_ERR_INVALID_ARG: return "invalid argument";
+    case OMNI_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case OMNI_ERR_WORKSPACE: return "workspace too small";
+    case OMNI_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* omni_last_error(void) { return g_err; }
+
+int omni_abi_version(void) { return OMNI_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Expert-centric scheduling on gfx950.
+//
+// OmniMoE digest (paper.rainbus.top), method paragraph, step 3: the L*K
+// routing tasks are sorted by expert id into contiguous groups of size B,
+// group id first, token id second; gist.science resume section 2.2: groups
+// are contiguous ranges of expert ids.
+//
+// Task m = t*K + k lists the tasks token-major, so the task order already
+// sorts by (token, m).  A STABLE sort of the tasks by group id alone
+// therefore yields the order (group, token, m): the key needs only
+// ceil(log2 G) bits.  It is an LSD radix sort with up to 8-bit digits:
+//   sched_hist     per-tile digit histograms (digit-major table)
+//   sched_scan     exclusive scan of that table (one workgroup)
+//   sched_scatter  stable scatter: in-tile ranks from wave ballots
+// followed by sched_offsets, which turns the sorted group ids into
+// group_off[q] = first sorted position whose group is >= q.
+
+#include "omni_internal.h"
+
+namespace omni {
+namespace {
+
+constexpr int SCHED_THREADS = 256;
+constexpr int SCHED_ROUNDS = 8;  // elements per tile = 256 * 8
+constexpr int SCHED_TILE = SCHED_THREADS * SCHED_ROUNDS;
+
+__device__ __forceinline__ int load_key(const int32_t* __restrict__ idx,
+                                        const int32_t* __restrict__ keys_in, int p, int B) {
+  return keys_in ? keys_in[p] : idx[p] / B;
+}
+
+__global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ keys_in,
+                                                            int M, int B, int shift, int radix,
+                                                            int ntiles, int* __restrict__ hist) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x, tile = blockIdx.x;
+  if (tid < radix) h[tid] = 0;
+  __syncthreads();
+  const int base = tile * SCHED_TILE;
+  for (int r = 0; r < SCHED_ROUNDS; ++r) {
+    const int p = base + r * SCHED_THREADS + tid;
+    if (p < M) atomicAdd(&h[(load_key(idx, keys_in, p, B) >> shift) & (radix - 1)], 1);
+  }
+  __syncthreads();
+  if (tid < radix) hist[tid * ntiles + tile] = h[tid];
+}
+
+// Exclusive scan of n ints in place by one 1024-thread workgroup.
+__global__ __launch_bounds__(1024) void sched_scan(int* __restrict__ a, int n) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int i = lo; i < hi; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
+    const int32_t* __restrict__ vals_in, int M, int B, int shift, int radix, int ntiles,
+    const int* __restrict__ hist, int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+  __shared__ int run[256];
+  __shared__ int wcnt[SCHED_THREADS / 64][256];
+  const int tid = threadIdx.x, tile = blockIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int dbits = 31 - __clz(radix);
+  if (tid < radix) {
+    run[tid] = hist[tid * ntiles + tile];
+#pragma unroll
+    for (int w = 0; w < SCHED_THREADS / 64; ++w) wcnt[w][tid] = 0;
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int base = tile * SCHED_TILE;
+  for (int r = 0; r < SCHED_ROUNDS; ++r) {
+    const int p = base + r * SCHED_THREADS + tid;
+    const bool act = p < M;
+    int key = 0, val = 0, dig = 0;
+    if (act) {
+      key = load_key(idx, keys_in, p, B);
+      val = vals_in ? vals_in[p] : p;
+      dig = (key >> shift) & (radix - 1);
+    }
+    // lanes of this wave holding the same digit (ballot per digit bit)
+    unsigned long long peers = __ballot(act);
+    for (int b = 0; b < dbits; ++b) {
+      const unsigned long long m = __ballot((dig >> b) & 1);
+      peers &= ((dig >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    if (act && (peers >> lane) == 1ull) wcnt[wave][dig] = __popcll(peers);  // highest peer
+    __syncthreads();
+    if (act) {
+      int pos = run[dig] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][dig];
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    if (tid < radix) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < SCHED_THREADS / 64; ++w) {
+        s += wcnt[w][tid];
+        wcnt[w][tid] = 0;
+      }
+      run[tid] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// group_off[q] = first sorted position p with key[p] >= q, for q in [0, G].
+__global__ void sched_offsets(const int32_t* __restrict__ keys, int M, int G,
+                              int32_t* __restrict__ off) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p > M) return;
+  // ids outside [0, N) break the precondition; clamping keeps the writes in
+  // bounds (the offsets are then meaningless, but nothing is corrupted)
+  const int prev = p == 0 ? -1 : max(-1, min(G, keys[p - 1]));
+  const int cur = p == M ? G : max(-1, min(G, keys[p]));
+  for (int q = prev + 1; q <= cur; ++q) off[q] = p;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B) {
+  SchedPlan p{};
+  p.M = (int)(L * K);
+  p.G = (int)((N + B - 1) / B);
+  int bits = 1;
+  while (bits < 31 && (1ll << bits) < p.G) ++bits;  // groups 0 .. G-1 fit in `bits`
+  p.passes = (bits + 7) / 8;
+  p.digit_bits = (bits + p.passes - 1) / p.passes;
+  p.ntiles = (p.M + SCHED_TILE - 1) / SCHED_TILE;
+  const size_t arr = align256((size_t)p.M * 4);
+  p.off_keys_a = 0;
+  p.off_vals_a = arr;
+  p.off_keys_b = 2 * arr;
+  p.off_vals_b = 3 * arr;
+  p.off_hist = 4 * arr;
+  p.ws_bytes = p.off_hist + align256((size_t)(1 << p.digit_bits) * p.ntiles * 4);
+  return p;
+}
+
+hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  int32_t* ka = (int32_t*)(w + plan.off_keys_a);
+  int32_t* va = (int32_t*)(w + plan.off_vals_a);
+  int32_t* kb = (int32_t*)(w + plan.off_keys_b);
+  int32_t* vb = (int32_t*)(w + plan.off_vals_b);
+  int* hist = (int*)(w + plan.off_hist);
+  const int radix = 1 << plan.digit_bits;
+  const int32_t* kin = nullptr;  // pass 0 derives keys from idx
+  const int32_t* vin = nullptr;  // pass 0 values are the task ids
+  for (int pass = 0; pass < plan.passes; ++pass) {
+    const bool last = pass + 1 == plan.passes;
+    int32_t* kout = (pass & 1) ? kb : ka;
+    int32_t* vout = last ? perm : ((pass & 1) ? vb : va);
+    const int shift = pass * plan.digit_bits;
+    hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M, B,
+                       shift, radix, plan.ntiles, hist);
+    hipLaunchKernelGGL(sched_scan, dim3(1), dim3(1024), 0, s, hist, radix * plan.ntiles);
+    hipLaunchKernelGGL(sched_scatter, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, vin,
+                       M, B, shift, radix, plan.ntiles, hist, kout, vout);
+    kin = kout;
+    vin = vout;
+  }
+  hipLaunchKernelGGL(sched_offsets, dim3((M + 1 + 255) / 256), dim3(256), 0, s, kin, M, G,
+                     group_off);
+  return hipGetLastError();
+}
+
+}  // namespace omni

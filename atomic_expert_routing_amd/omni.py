@@ -1,0 +1,219 @@
+"""ctypes binding of libomni.so (include/omni.h), same names as the C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and sizes go to the C entry points, and
+the call is enqueued on torch's current HIP stream.  Outputs and workspaces
+that the caller does not pass are allocated with torch (device memory is the
+only thing PyTorch provides here).  Every step of the routed branch runs in
+the library's HIP kernels; if the library is missing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
+_ABI_VERSION = 1
+
+OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
+OMNI_F32, OMNI_BF16 = 0, 1
+OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
+EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward", "omni_workspace_bytes",
+            "omni_status_string", "omni_last_error", "omni_abi_version")
+
+
+class OmniError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {detail} (status {status})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Open libomni.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m atomic_expert_routing_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.omni_router.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                vp, vp, vp, vp, sz, vp]
+    lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                        ctypes.c_int, vp, vp, sz, vp]
+    lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, ctypes.POINTER(sz)]
+    for f in ("omni_router", "omni_schedule", "omni_expert_forward", "omni_workspace_bytes"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.omni_status_string.argtypes = [ctypes.c_int]
+    lib.omni_status_string.restype = ctypes.c_char_p
+    lib.omni_last_error.argtypes = []
+    lib.omni_last_error.restype = ctypes.c_char_p
+    lib.omni_abi_version.argtypes = []
+    lib.omni_abi_version.restype = ctypes.c_int
+    if lib.omni_abi_version() != _ABI_VERSION:
+        raise RuntimeError(f"{_LIB_PATH}: ABI version {lib.omni_abi_version()} != {_ABI_VERSION}; rebuild")
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != OMNI_OK:
+        lib = library()
+        raise OmniError(status, where, lib.omni_last_error().decode() or
+                        lib.omni_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return OMNI_BF16
+    if t.dtype == torch.float32:
+        return OMNI_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def omni_workspace_bytes(op: int, L=1, d=8, Nr=1, Nc=1, K=1, N=1, B=1, dtype=OMNI_BF16) -> int:
+    out = ctypes.c_size_t(0)
+    _check(library().omni_workspace_bytes(op, L, d, Nr, Nc, K, N, B, dtype, ctypes.byref(out)),
+           "omni_workspace_bytes")
+    return out.value
+
+
+def _workspace(ws, need: int, device) -> tuple[int, int]:
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(ws, "ws")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def omni_router(x, Wr, Wc, K: int, idx=None, score=None, gate=None, ws=None, stream=None):
+    """Cartesian Product Router -> (idx [L,K] int32, score [L,K] f32, gate [L,K] f32)."""
+    L, d = x.shape
+    Nr, Nc = Wr.shape[0], Wc.shape[0]
+    dt = _dtype_code(x)
+    px = _dev(x, "x")
+    pr = _dev(Wr, "Wr", x.dtype, (Nr, d))
+    pc = _dev(Wc, "Wc", x.dtype, (Nc, d))
+    kw = dict(device=x.device)
+    idx = torch.empty((L, K), dtype=torch.int32, **kw) if idx is None else idx
+    score = torch.empty((L, K), dtype=torch.float32, **kw) if score is None else score
+    gate = torch.empty((L, K), dtype=torch.float32, **kw) if gate is None else gate
+    pi = _dev(idx, "idx", torch.int32, (L, K))
+    ps = _dev(score, "score", torch.float32, (L, K))
+    pg = _dev(gate, "gate", torch.float32, (L, K))
+    if ws is None:
+        need = omni_workspace_bytes(OMNI_OP_ROUTER, L, d, Nr, Nc, K, Nr * Nc, 1, dt)
+    else:
+        need = 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_router(px, pr, pc, L, d, Nr, Nc, K, dt, pi, ps, pg, pw, nw,
+                                 _stream(stream)), "omni_router")
+    return idx, score, gate
+
+
+def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, stream=None):
+    """Expert-centric schedule -> (perm [L*K] int32, group_off [G+1] int32)."""
+    L, K = idx.shape
+    G = -(-N // B)
+    pi = _dev(idx, "idx", torch.int32)
+    kw = dict(device=idx.device, dtype=torch.int32)
+    perm = torch.empty((L * K,), **kw) if perm is None else perm
+    group_off = torch.empty((G + 1,), **kw) if group_off is None else group_off
+    pp = _dev(perm, "perm", torch.int32, (L * K,))
+    po = _dev(group_off, "group_off", torch.int32, (G + 1,))
+    need = omni_workspace_bytes(OMNI_OP_SCHEDULE, L, 8, 1, 1, K, N, B) if ws is None else 0
+    pw, nw = _workspace(ws, need, idx.device)
+    _check(library().omni_schedule(pi, L, K, N, B, pp, po, pw, nw, _stream(stream)),
+           "omni_schedule")
+    return perm, group_off
+
+
+def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None):
+    """Dynamic Expert Assembly over the schedule -> y [L, d] float32."""
+    L, d = x.shape
+    N = W.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    px = _dev(x, "x")
+    pW = _dev(W, "W", x.dtype, (N, d))
+    pV = _dev(V, "V", x.dtype, (N, d))
+    pi = _dev(idx, "idx", torch.int32, (L, K))
+    pg = _dev(gate, "gate", torch.float32, (L, K))
+    pp = _dev(perm, "perm", torch.int32, (L * K,))
+    y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
+    py = _dev(y, "y", torch.float32, (L, d))
+    need = omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, L, d, N, K, dt, py, pw, nw,
+                                         _stream(stream)), "omni_expert_forward")
+    return y
+
+
+class RoutedBranch:
+    """Preallocated outputs and workspaces for repeated routed-branch forwards.
+
+    One instance per (shape, dtype): `forward(x, Wr, Wc, W, V)` enqueues the
+    three C calls on the current stream and allocates nothing.
+    """
+
+    def __init__(self, L, d, Nr, Nc, K, B, dtype=torch.bfloat16, device="cuda"):
+        self.L, self.d, self.Nr, self.Nc, self.K, self.B = L, d, Nr, Nc, K, B
+        self.N = Nr * Nc
+        self.G = -(-self.N // B)
+        dt = OMNI_BF16 if dtype == torch.bfloat16 else OMNI_F32
+        i32, f32 = torch.int32, torch.float32
+        kw = dict(device=device)
+        self.idx = torch.empty((L, K), dtype=i32, **kw)
+        self.score = torch.empty((L, K), dtype=f32, **kw)
+        self.gate = torch.empty((L, K), dtype=f32, **kw)
+        self.perm = torch.empty((L * K,), dtype=i32, **kw)
+        self.group_off = torch.empty((self.G + 1,), dtype=i32, **kw)
+        self.y = torch.empty((L, d), dtype=f32, **kw)
+        sizes = [omni_workspace_bytes(OMNI_OP_ROUTER, L, d, Nr, Nc, K, self.N, B, dt),
+                 omni_workspace_bytes(OMNI_OP_SCHEDULE, L, d, Nr, Nc, K, self.N, B, dt),
+                 omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, Nr, Nc, K, self.N, B, dt)]
+        # the three calls run in order on one stream, so they share one workspace
+        self.ws = torch.empty(max(sizes), dtype=torch.uint8, **kw)
+
+    def router(self, x, Wr, Wc, stream=None):
+        return omni_router(x, Wr, Wc, self.K, self.idx, self.score, self.gate, self.ws, stream)
+
+    def schedule(self, stream=None):
+        return omni_schedule(self.idx, self.N, self.B, self.perm, self.group_off, self.ws, stream)
+
+    def expert_forward(self, x, W, V, stream=None):
+        return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.y, self.ws, stream)
+
+    def forward(self, x, Wr, Wc, W, V, stream=None):
+        self.router(x, Wr, Wc, stream)
+        self.schedule(stream)
+        return self.expert_forward(x, W, V, stream)

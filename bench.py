@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Routed-branch forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole routed branch (omni_router, omni_schedule,
+omni_expert_forward) over one batch of seeded synthetic inputs that are
+already resident in HBM.  The default workload is 4096 tokens over 1.7M
+atomic experts (d = 2048, N_r = N_c = 1304, K = B = 128, bf16 inputs, fp32
+arithmetic).  Prints ONE JSON line.
+
+Timing: W untimed steps, then exactly K steps between two device
+synchronisations (wall clock), with HIP events (torch.cuda.Event on the
+stream the library launches on) around each call for the per-stage split.
+The roofline entry covers the expert-assembly call (its two kernels:
+expert_act and expert_out), whose algorithmic bytes are the unique W and V
+rows gathered, x read once, y written once and 12 bytes of task metadata
+per task; the unique expert count is taken from the step's own ids.
+
+cpu_baseline: the float64 CPU oracle timed on this host on a bounded sample
+of the same workload's tokens, scaled to the full token count.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per 4096-token routed-branch forward (router+sched+experts); % HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, w, n_tok, seed):
+    """Time the oracle (as it stands) on n_tok sampled tokens; scale to L."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    from oracle import omni_oracle as O
+
+    rs = np.random.Generator(np.random.PCG64(seed + 1))
+    toks = np.sort(rs.choice(w.L, size=min(n_tok, w.L), replace=False))
+    # setup (untimed): bring the sampled inputs and the router weights to host
+    x = inp["x"][torch.as_tensor(toks, device=inp["x"].device)].to("cpu", torch.float64).numpy()
+    Wr = inp["Wr"].to("cpu", torch.float64).numpy()
+    Wc = inp["Wc"].to("cpu", torch.float64).numpy()
+    t0 = time.perf_counter()
+    idx, score, gate, _, _ = O.route(x, Wr, Wc, w.K)
+    t_route = time.perf_counter() - t0
+    # setup (untimed): the W and V rows those routes need
+    uids = np.unique(idx)
+    ids_dev = torch.as_tensor(uids, device=inp["W"].device)
+    rows_W = inp["W"].index_select(0, ids_dev).to("cpu", torch.float64).numpy()
+    rows_V = inp["V"].index_select(0, ids_dev).to("cpu", torch.float64).numpy()
+
+    class Rows:
+        def __init__(self, rows):
+            self.rows = rows
+
+        def __getitem__(self, ids):
+            return self.rows[np.searchsorted(uids, ids)]
+
+    t0 = time.perf_counter()
+    perm, off = O.schedule(idx, w.N, w.B)
+    O.assemble_expert_centric(x, Rows(rows_W), Rows(rows_V), idx, gate, perm, off)
+    t_rest = time.perf_counter() - t0
+    secs = t_route + t_rest
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    cores = max([p.get("num_threads", 1) for p in blas] + [1])
+    return {
+        "value": round(secs * 1e3 * w.L / len(toks), 3),
+        "unit": "ms",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{len(toks)} of {w.L} tokens (seeded), router+schedule+expert-centric "
+                   f"assembly in float64, {secs:.2f} s measured, scaled x{w.L / len(toks):g}; "
+                   f"host affinity {len(os.sched_getaffinity(0))} cpus"),
+        "stages_s": {"route": round(t_route, 3), "schedule+assembly": round(t_rest, 3)},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the routed "
+              "branch here is a single-GPU kernel path; see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from atomic_expert_routing_amd import omni, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    log(f"[bench] workload {w.name}: generating inputs on the GPU")
+    inp = synth.make_inputs(w, seed=args.seed, device="cuda")
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        br.router(inp["x"], inp["Wr"], inp["Wc"])
+        if ev is not None:
+            ev[1].record()
+        br.schedule()
+        if ev is not None:
+            ev[2].record()
+        br.expert_forward(inp["x"], inp["W"], inp["V"])
+        if ev is not None:
+            ev[3].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def med(a, b):
+        return statistics.median(e[a].elapsed_time(e[b]) for e in evs)
+
+    router_ms, sched_ms, expert_ms = med(0, 1), med(1, 2), med(2, 3)
+    expert_mean_ms = statistics.fmean(e[2].elapsed_time(e[3]) for e in evs)
+    step_ev_ms = med(0, 3)
+
+    # algorithmic bytes of one expert-assembly call (one launch of the pair)
+    U = int(torch.unique(br.idx).numel())
+    es = 2 if w.dtype == "bf16" else 4
+    expert_bytes = U * 2 * w.d * es + w.L * w.d * es + w.L * w.d * 4 + w.M * 12
+    achieved = expert_bytes / (expert_mean_ms * 1e-3) / 1e9
+    router_bytes = (w.L + w.Nr + w.Nc) * w.d * es + w.M * 12
+    sched_bytes = w.M * 4 + w.M * 4 + (w.G + 1) * 4
+    branch_bytes = expert_bytes + router_bytes + sched_bytes
+    router_flops = 2.0 * w.L * w.d * (w.Nr + w.Nc)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded Gaussian x and random-init W, V, W_r, W_c (no trained weights)",
+        "config": {**w.describe(), "parallelism": "single GPU"},
+        "tokens_per_s": round(w.L / (ms_step * 1e-3), 1),
+        "branch_hbm_frac": round(branch_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stages_ms_median": {"router": round(router_ms, 4), "schedule": round(sched_ms, 4),
+                             "expert_forward": round(expert_ms, 4),
+                             "step_events": round(step_ev_ms, 4)},
+        "unique_experts": U,
+        "roofline": {
+            "kernel": "omni_expert_forward (expert_act + expert_out)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": expert_bytes,
+            "mean_ms": round(expert_mean_ms, 4),
+        },
+        "router_gemm_flops": router_flops,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_sample_tokens, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

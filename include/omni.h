@@ -1,0 +1,171 @@
+/*
+ * omni.h - C ABI of libomni.so, the MI355X (gfx950) routed-branch forward of
+ * OmniMoE ("OmniMoE: An Efficient MoE by Orchestrating Atomic Experts at
+ * Scale", arXiv 2602.05711).
+ *
+ * The routed branch runs in three calls on one HIP stream:
+ *   omni_router          Cartesian Product Router: ids, scores, gates
+ *   omni_schedule        expert-centric schedule: sorted tasks, group offsets
+ *   omni_expert_forward  Dynamic Expert Assembly: y
+ *
+ * Conventions shared by every call
+ *   - Every array pointer is DEVICE memory owned by the caller, row-major and
+ *     contiguous, with a 16-byte-aligned base.  The library never allocates,
+ *     frees or synchronises; scratch memory comes in through (ws, ws_bytes),
+ *     sized by omni_workspace_bytes, device memory, 256-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued on it; results are ready when the stream reaches that point.
+ *   - x, W_r, W_c, W and V share one dtype (omni_dtype).  Arithmetic is fp32
+ *     (bf16 values are widened exactly; products accumulate in fp32).
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is enqueued and no output is touched.  omni_last_error()
+ *     returns a message for the calling thread's last failed call.
+ *     OMNI_ERR_HIP reports a launch error; faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Expert ids in idx must lie in [0, N) (a precondition, not checked on
+ *     the device).
+ *   - Calls are reentrant; two calls that share output or workspace buffers
+ *     must be ordered by the caller (same stream, or events).
+ */
+#ifndef OMNI_H
+#define OMNI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OMNI_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define OMNI_API __attribute__((visibility("default")))
+#else
+#define OMNI_API
+#endif
+
+typedef enum {
+  OMNI_OK = 0,
+  OMNI_ERR_INVALID_ARG = 1, /* null pointer, non-positive or inconsistent size */
+  OMNI_ERR_UNSUPPORTED = 2, /* valid request beyond the compiled limits below */
+  OMNI_ERR_WORKSPACE = 3,   /* ws_bytes below omni_workspace_bytes() */
+  OMNI_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} omni_status;
+
+typedef enum { OMNI_F32 = 0, OMNI_BF16 = 1 } omni_dtype;
+
+typedef enum {
+  OMNI_OP_ROUTER = 0,
+  OMNI_OP_SCHEDULE = 1,
+  OMNI_OP_EXPERT_FORWARD = 2
+} omni_op;
+
+/* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
+#define OMNI_MAX_GRID_SIDE 4096 /* N_r, N_c */
+#define OMNI_MAX_K 512
+#define OMNI_MAX_D_BF16 4096 /* d for bf16 inputs */
+#define OMNI_MAX_D_F32 2048  /* d for fp32 inputs */
+
+/*
+ * omni_router - Cartesian Product Router.
+ * Source: OmniMoE digest (paper.rainbus.top), method paragraph, step 2;
+ * gist.science resume section 2.2 ("Cartesian product router").
+ *
+ * For each token t (row of x):
+ *   s_r = x_t W_r,  s_c = x_t W_c                       (row / column logits)
+ *   p_r = LogSoftmax(s_r),  p_c = LogSoftmax(s_c)
+ *   S_ij = p_r[i] + p_c[j] over the implicit N_r x N_c grid (never built)
+ *   the K best grid cells under (S descending, n ascending), n = i*N_c + j
+ *   gate = softmax of the K selected S
+ *
+ *   x      [L, d]     dtype dt
+ *   Wr     [N_r, d]   dtype dt   row i is grid row i's projection vector
+ *   Wc     [N_c, d]   dtype dt   row j is grid column j's projection vector
+ *   idx    [L, K]     int32  out  expert ids, each row ordered by (S desc, n asc)
+ *   score  [L, K]     fp32   out  S of each selected id
+ *   gate   [L, K]     fp32   out  softmax over the row's K scores
+ * Requires 1 <= K <= N_r*N_c, K <= OMNI_MAX_K, N_r, N_c <= OMNI_MAX_GRID_SIDE,
+ * d % 8 == 0, d <= OMNI_MAX_D_BF16 (bf16) or OMNI_MAX_D_F32 (fp32),
+ * L*K < 2^31, N_r*N_c < 2^31.
+ * Workspace: fp32 logits [L, N_r + N_c].
+ */
+OMNI_API omni_status omni_router(const void* x, const void* Wr, const void* Wc,
+                        int64_t L, int64_t d, int64_t Nr, int64_t Nc,
+                        int64_t K, omni_dtype dt,
+                        int32_t* idx, float* score, float* gate,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_schedule - expert-centric scheduling.
+ * Source: OmniMoE digest, method paragraph, step 3 (task collection, sort by
+ * expert id into contiguous groups of size B, group id primary and token id
+ * secondary key); gist.science resume section 2.2 (groups are contiguous
+ * ranges of expert ids, tasks sorted by token id inside each group).
+ *
+ * Task m = t*K + k is (token t, expert idx[m]); its group is idx[m] / B.
+ *   perm       [L*K]    int32 out  task ids sorted by (group, token, m)
+ *   group_off  [G+1]    int32 out  G = ceil(N/B); group_off[q] = number of
+ *                                  tasks whose group is < q, so group q's
+ *                                  tasks are perm[group_off[q] .. group_off[q+1])
+ *                                  (empty for an inactive group)
+ * Bit-exact and deterministic.  Requires N >= 1, B >= 1, L*K < 2^31,
+ * N < 2^31.  Workspace: sort buffers, O(L*K) int32.
+ */
+OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
+                          int64_t N, int64_t B,
+                          int32_t* perm, int32_t* group_off,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_expert_forward - Dynamic Expert Assembly over the schedule.
+ * Source: OmniMoE digest, method paragraph, step 1 (global matrices
+ * W = [w_in^0 .. w_in^{N-1}]^T and V likewise; y = (g . sigma(x w_x^T)) v_x)
+ * and step 3 (per active group O_q = (G_q . sigma(X_q W_q^T)) V_q);
+ * gist.science resume section 2.1.
+ *
+ *   x     [L, d]  dtype dt
+ *   W, V  [N, d]  dtype dt    row e holds atomic expert e's input / output vector
+ *   idx   [L, K]  int32       expert ids (from omni_router)
+ *   gate  [L, K]  fp32        gates      (from omni_router)
+ *   perm  [L*K]   int32       schedule   (from omni_schedule)
+ *   y     [L, d]  fp32 out    y_t = sum_k gate[t,k] * SiLU(x_t . W[idx[t,k]]) * V[idx[t,k]]
+ *                             fully overwritten (no accumulation into old y)
+ * SiLU(h) = h / (1 + exp(-h)).  The activation pass walks the tasks in
+ * schedule order (expert-centric: a group's weight rows are read once and
+ * reused by its tokens); the output pass sums each token's K terms in k
+ * order without atomics, so y is deterministic.
+ * Requires d % 8 == 0, d <= OMNI_MAX_D_BF16 (bf16) or OMNI_MAX_D_F32 (fp32),
+ * L*K < 2^31, N < 2^31.  Workspace: fp32 activations [L*K].
+ */
+OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const void* V,
+                                const int32_t* idx, const float* gate,
+                                const int32_t* perm,
+                                int64_t L, int64_t d, int64_t N, int64_t K,
+                                omni_dtype dt, float* y,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_workspace_bytes - workspace size needed by one call of `op` with
+ * these sizes (arguments an op does not use are ignored).  Writes *out.
+ * Returns the same validation status the call itself would return for the
+ * sizes (pointers are not checked).
+ */
+OMNI_API omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr,
+                                 int64_t Nc, int64_t K, int64_t N, int64_t B,
+                                 omni_dtype dt, size_t* out);
+
+/* Static description of a status code. */
+OMNI_API const char* omni_status_string(omni_status s);
+
+/* Detail message of the calling thread's last failed call ("" if none). */
+OMNI_API const char* omni_last_error(void);
+
+/* OMNI_ABI_VERSION of the built library. */
+OMNI_API int omni_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OMNI_H */

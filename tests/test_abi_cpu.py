@@ -1,0 +1,128 @@
+"""Host-side checks of libomni.so that need no GPU.
+
+The library must load, export every function include/omni.h declares, size
+workspaces, and reject invalid arguments before it touches the GPU (the
+validation runs on the host, so these calls never reach the HIP runtime).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from atomic_expert_routing_amd import omni
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "omni.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(omni._LIB_PATH),
+                                reason="libomni.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"OMNI_API\s+[\w\s\*]+?\b(omni_\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == set(omni.EXPORTED), names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = omni.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.omni_abi_version() == 1
+
+
+def test_status_strings():
+    lib = omni.library()
+    for s in range(5):
+        assert lib.omni_status_string(s).decode()
+    assert lib.omni_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_sizes():
+    # router: fp32 logits [L, N_r + N_c], 256-byte aligned
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER, L=4096, d=2048, Nr=1304, Nc=1304,
+                                     K=128) == 4096 * 2608 * 4
+    # expert forward: fp32 activations [L*K]
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4096, d=2048, K=128,
+                                     N=1700416) == 4096 * 128 * 4
+    # schedule: four O(M) int32 sort buffers plus the digit table
+    ws = omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=4096, K=128, N=1700416, B=128)
+    assert 4 * 4096 * 128 * 4 <= ws < 5 * 4096 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), omni.OMNI_ERR_INVALID_ARG),
+    (dict(K=0), omni.OMNI_ERR_INVALID_ARG),
+    (dict(d=12), omni.OMNI_ERR_UNSUPPORTED),
+    (dict(d=-8), omni.OMNI_ERR_INVALID_ARG),
+    (dict(d=8192), omni.OMNI_ERR_UNSUPPORTED),
+    (dict(Nr=0), omni.OMNI_ERR_INVALID_ARG),
+    (dict(Nr=5000), omni.OMNI_ERR_UNSUPPORTED),
+    (dict(K=17, Nr=4, Nc=4), omni.OMNI_ERR_INVALID_ARG),  # K > N_r*N_c
+    (dict(K=600, Nr=100, Nc=100), omni.OMNI_ERR_UNSUPPORTED),
+    (dict(L=2**30, K=4), omni.OMNI_ERR_UNSUPPORTED),  # L*K >= 2^31
+    (dict(dtype=7), omni.OMNI_ERR_INVALID_ARG),
+])
+def test_router_size_validation(kw, status):
+    args = dict(L=64, d=64, Nr=32, Nc=32, K=16, N=1024, B=16, dtype=omni.OMNI_BF16)
+    args.update(kw)
+    with pytest.raises(omni.OmniError) as e:
+        omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER, **args)
+    assert e.value.status == status
+
+
+def test_fp32_d_limit_is_lower():
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4, d=4096, K=2, N=8,
+                                     dtype=omni.OMNI_BF16) > 0
+    with pytest.raises(omni.OmniError) as e:
+        omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4, d=4096, K=2, N=8,
+                                  dtype=omni.OMNI_F32)
+    assert e.value.status == omni.OMNI_ERR_UNSUPPORTED
+
+
+def test_schedule_validation():
+    for kw in (dict(N=0), dict(B=0), dict(N=2**31)):
+        args = dict(L=4, K=2, N=100, B=8)
+        args.update(kw)
+        with pytest.raises(omni.OmniError):
+            omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, **args)
+    with pytest.raises(omni.OmniError):
+        omni.omni_workspace_bytes(7)
+
+
+def test_calls_reject_before_launch():
+    """Invalid calls return an error and a message without touching the GPU."""
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    # NULL output pointer
+    s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 2, omni.OMNI_F32, None, fake, fake,
+                        fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
+    # workspace too small
+    s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 2, omni.OMNI_F32, fake, fake, fake,
+                        fake, 16, None)
+    assert s == omni.OMNI_ERR_WORKSPACE and b"workspace" in lib.omni_last_error()
+    # misaligned workspace
+    s = lib.omni_schedule(fake, 4, 2, 10, 2, fake, fake, ctypes.c_void_p(4100), 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG
+    # misaligned x
+    s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, 4, 8, 10,
+                                2, omni.OMNI_BF16, fake, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG
+    # K larger than the grid
+    s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 5, omni.OMNI_F32, fake, fake, fake,
+                        fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"K" in lib.omni_last_error()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        omni.omni_router(x, torch.zeros(2, 8), torch.zeros(2, 8), 2)

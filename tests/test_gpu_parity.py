@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small and ragged cases are compared in full; the large workloads run in the
+launch configuration the benchmark times (RoutedBranch: one workspace, three
+calls on one stream) and are compared on sampled tokens (router, assembly)
+and in full (schedule).
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from atomic_expert_routing_amd import omni, synth
+from oracle import omni_oracle as O
+from parity import (DeviceRows, RTOL, RTOL_FP32_ARITH, check_schedule, check_topk, check_y,
+                    to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    omni.library()  # fails loudly if the HIP library is missing
+
+
+def run_branch(inp, w):
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
+    br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    torch.cuda.synchronize()
+    return br
+
+
+def full_check(w, inp_cpu):
+    """Whole-tensor comparison for a workload small enough for the oracle."""
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    say(f"case {w.name}")
+    br = run_branch(inp, w)
+    idx_o, score_o, gate_o, p_r, p_c = O.route(inp_cpu["x"], inp_cpu["Wr"], inp_cpu["Wc"], w.K)
+    swaps = check_topk(br.idx, br.score, br.gate, p_r, p_c, w.K)
+    check_schedule(br.idx, br.perm, br.group_off, w.N, w.B)
+    perm_o, off_o = O.schedule(to_np(br.idx).astype(np.int64), w.N, w.B)
+    y_o = O.assemble_expert_centric(inp_cpu["x"], inp_cpu["W"], inp_cpu["V"], to_np(br.idx),
+                                    to_np(br.gate), perm_o, off_o)
+    nrm, mx = check_y(br.y, y_o, min(RTOL[w.dtype], RTOL_FP32_ARITH))
+    say(f"  swaps={swaps} y_err norm={nrm:.2e} max={mx:.2e}")
+    return br, swaps
+
+
+def test_tiny_workload_matches_oracle_and_bruteforce():
+    w = synth.WORKLOADS[synth.TINY]
+    inp = synth.make_inputs(w, seed=0)
+    br, swaps = full_check(w, inp)
+    # on this small grid the explicit brute force is affordable too: the same
+    # rule must hold against it
+    _, _, _, p_r, p_c = O.route(inp["x"], inp["Wr"], inp["Wc"], w.K, method="explicit")
+    idx_e, _ = O.topk_explicit(p_r, p_c, w.K)
+    same = (np.sort(to_np(br.idx), 1) == np.sort(idx_e, 1)).all(1).mean()
+    say(f"  tokens whose id set equals the brute-force set: {same:.3f} (swaps {swaps})")
+
+
+RAGGED = [
+    # L, d, Nr, Nc, K, B, dtype
+    (1, 8, 1, 1, 1, 1, "f32"),            # one token, one expert
+    (3, 24, 5, 7, 35, 4, "f32"),          # K = N: every grid cell
+    (5, 16, 1, 40, 9, 6, "f32"),          # single grid row
+    (130, 72, 37, 29, 50, 7, "bf16"),     # K > N_r and K > N_c; ragged tiles
+    (257, 136, 130, 200, 64, 100, "bf16"),
+    (200, 520, 300, 301, 128, 128, "bf16"),  # d crosses a 512-column chunk
+    (300, 64, 50, 50, 37, 3, "f32"),      # several schedule tiles, ragged tail
+    (64, 64, 32, 32, 16, 1, "bf16"),      # B = 1: one group per expert
+    (64, 64, 32, 32, 16, 5000, "bf16"),   # B >= N: one group
+    (40, 64, 600, 700, 512, 512, "bf16"),  # K at its limit
+    (20, 64, 4096, 3, 100, 33, "f32"),    # grid side at its limit
+    (16, 4096, 64, 64, 32, 64, "bf16"),   # d at its bf16 limit
+    (24, 2048, 40, 40, 20, 16, "f32"),    # d at its fp32 limit
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "L{}_d{}_{}x{}_K{}_B{}_{}".format(*c))
+def test_ragged_and_edge_cases(case):
+    L, d, Nr, Nc, K, B, dt = case
+    w, inp = synth.make_case(L, d, Nr, Nc, K, B, dt, seed=zlib.crc32(repr(case).encode()) % 1000)
+    full_check(w, inp)
+
+
+def test_schedule_on_oracle_routing_is_bit_exact():
+    # the schedule fed with the oracle's own ids (not the GPU router's)
+    w = synth.WORKLOADS[synth.TINY]
+    inp = synth.make_inputs(w, seed=3)
+    idx_o, _, _, _, _ = O.route(inp["x"], inp["Wr"], inp["Wc"], w.K)
+    for B in (1, 3, 16, 64, 1000, 2000):
+        say(f"schedule oracle ids B={B}")
+        idx = torch.as_tensor(idx_o, dtype=torch.int32, device="cuda")
+        perm, off = omni.omni_schedule(idx, w.N, B)
+        torch.cuda.synchronize()
+        check_schedule(idx_o, perm, off, w.N, B)
+
+
+def test_expert_forward_on_oracle_routing():
+    w = synth.WORKLOADS[synth.TINY]
+    inp = synth.make_inputs(w, seed=4)
+    out = O.routed_forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"], w.K, w.B)
+    g = {k: v.cuda() for k, v in inp.items()}
+    idx = torch.as_tensor(out["idx"], dtype=torch.int32, device="cuda")
+    gate = torch.as_tensor(out["gate"], dtype=torch.float32, device="cuda")
+    perm = torch.as_tensor(out["perm"], dtype=torch.int32, device="cuda")
+    say("expert forward on oracle routing")
+    y = omni.omni_expert_forward(g["x"], g["W"], g["V"], idx, gate, perm)
+    torch.cuda.synchronize()
+    # the gate went through fp32 on its way in: compare with the oracle's y
+    # for the same fp32 gate values
+    y_o = O.assemble_token_centric(inp["x"], inp["W"], inp["V"], out["idx"], to_np(gate))
+    check_y(y, y_o, RTOL["f32"])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = synth.WORKLOADS[synth.TINY]
+    inp = {k: v.cuda() for k, v in synth.make_inputs(w, seed=5).items()}
+    say("determinism")
+    ref = run_branch(inp, w)
+    snap = [t.clone() for t in (ref.idx, ref.score, ref.gate, ref.perm, ref.group_off, ref.y)]
+    for _ in range(10):
+        ref.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    torch.cuda.synchronize()
+    for a, b in zip(snap, (ref.idx, ref.score, ref.gate, ref.perm, ref.group_off, ref.y)):
+        assert torch.equal(a, b)
+
+
+def test_y_is_overwritten_not_accumulated():
+    w = synth.WORKLOADS[synth.TINY]
+    inp = {k: v.cuda() for k, v in synth.make_inputs(w, seed=6).items()}
+    say("y overwrite")
+    br = run_branch(inp, w)
+    y1 = br.y.clone()
+    br.y.fill_(123.0)
+    br.expert_forward(inp["x"], inp["W"], inp["V"])
+    torch.cuda.synchronize()
+    assert torch.equal(br.y, y1)
+
+
+# ------------------------------------------------------------ full-size workloads
+
+LARGE = ["L4096_N280900_d768", "L4096_N1048576_d1024", synth.HEADLINE,
+         "skewed_L16384_N1700416_d2048"]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_full_size_workload_sampled(name):
+    w = synth.WORKLOADS[name]
+    say(f"full-size {name}: generating inputs")
+    inp = synth.make_inputs(w, seed=0, device="cuda")
+    say(f"full-size {name}: routed forward")
+    br = run_branch(inp, w)
+    # schedule: whole arrays, bit-exact
+    check_schedule(br.idx, br.perm, br.group_off, w.N, w.B)
+    # router and assembly: sampled tokens (first, last and spread)
+    rs = np.random.Generator(np.random.PCG64(7))
+    toks = np.unique(np.concatenate([[0, w.L - 1], rs.choice(w.L, 30, replace=False)]))
+    xs = to_np(inp["x"][torch.as_tensor(toks, device="cuda")])
+    _, _, _, p_r, p_c = O.route(xs, inp["Wr"], inp["Wc"], w.K)
+    idx = to_np(br.idx)[toks]
+    swaps = check_topk(idx, to_np(br.score)[toks], to_np(br.gate)[toks], p_r, p_c, w.K)
+    y_o = O.assemble_token_centric(xs, DeviceRows(inp["W"]), DeviceRows(inp["V"]),
+                                   idx, to_np(br.gate)[toks])
+    nrm, mx = check_y(to_np(br.y)[toks], y_o, min(RTOL[w.dtype], RTOL_FP32_ARITH))
+    say(f"  swaps={swaps} over {len(toks)} tokens; y_err norm={nrm:.2e} max={mx:.2e}")
+    del inp, br
+    torch.cuda.empty_cache()
