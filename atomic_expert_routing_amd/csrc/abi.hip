@@ -81,6 +81,7 @@ omni_status expert_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt,
   omni_status s;
   if ((s = check_dtype_d(dt, d)) != OMNI_OK) return s;
   if ((s = check_tasks(L, K)) != OMNI_OK) return s;
+  if (K > OMNI_MAX_K) return fail(OMNI_ERR_UNSUPPORTED, "K = %lld exceeds %d", (long long)K, OMNI_MAX_K);
   if (N <= 0) return fail(OMNI_ERR_INVALID_ARG, "N must be positive (got %lld)", (long long)N);
   if (N > I32_LIMIT) return fail(OMNI_ERR_UNSUPPORTED, "N = %lld exceeds 2^31-1", (long long)N);
   *out = align256((size_t)L * (size_t)K * 4);

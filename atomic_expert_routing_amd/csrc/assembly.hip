@@ -1,28 +1,26 @@
 // Dynamic Expert Assembly on gfx950.
 //
-// OmniMoE digest (paper.rainbus.top), method paragraph, step 1: each atomic
-// expert e is a pair of d-vectors (row e of W, row e of V) computing
-// sigma(x w_e^T) v_e; step 3: every active group q computes
+// OmniMoE digest (paper.rainbus.top), method paragraph, step 1: atomic expert
+// e is a pair of d-vectors (row e of W, row e of V) computing
+// sigma(x w_e^T) v_e; step 3: each active group q computes
 // O_q = (G_q . sigma(X_q W_q^T)) V_q over its scheduled tasks.
 //
-// The product is split in two passes so that y needs no atomics:
+// The product runs as two passes so that y needs no atomics:
 //   expert_act  walks the tasks in schedule order (groups of B consecutive
-//               experts, tokens ascending inside a group) and computes the
-//               gated activation a_m = g_m * SiLU(x_t . W[e_m]) of every task:
-//               the (G_q . sigma(X_q W_q^T)) factor.  Consecutive tasks reuse
-//               the same W rows (same group) and x rows (same token).
+//               experts, tokens ascending inside a group) and computes every
+//               task's gated activation a_m = g_m * SiLU(x_t . W[e_m]): the
+//               (G_q . sigma(X_q W_q^T)) factor of the group product.
 //   expert_out  y_t = sum_k a_{t,k} V[e_{t,k}]: the product with V_q, summed
-//               per token in k order by the thread that owns y_t's columns.
-// fp32 atomics on MI355X run at a few hundred G ops/s, far below what a
-// scatter-add of every group's O_q rows into y would need; the owner-computes
-// sum writes each y element exactly once and is deterministic.
+//               per token in k order by the threads that own y_t's columns.
+// fp32 atomics on MI355X sustain a few hundred G ops/s, far below what a
+// scatter-add of every group's O_q rows into y would need (about 2 ms at
+// 4096 tokens x 128 experts x d = 2048); the owner-computes sum writes each
+// y element once and is deterministic.
 
 #include "omni_internal.h"
 
 namespace omni {
 namespace {
-
-constexpr int ACT_TPW = 16;  // tasks per wave in expert_act
 
 template <bool BF16>
 struct Vec;
@@ -62,112 +60,149 @@ struct Vec<false> {  // 4 fp32 per 16-byte load
   }
 };
 
-__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ __forceinline__ float readlane(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+// Non-temporal 16-byte load: weight rows are streamed, not reused from L2.
+__device__ __forceinline__ u32x4 ld16_nt(const char* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
 }
 
-// One wave per ACT_TPW consecutive scheduled tasks.  A row of d elements is
-// NCH chunks of 64 lanes x 16 bytes; lane `lane` holds bytes [16*lane, +16)
-// of each chunk.  The task metadata is fetched once per wave (one task per
-// lane) and broadcast; the next task's W row (and x row, when the token
-// changes) is in flight while the current one is reduced.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// ------------------------------------------------------------------ expert_act
+// The 8 XCDs of an MI355X each have their own L2 and workgroup i runs on XCD
+// i % 8.  The scheduled task stream is cut into chunks of ACT_CHUNK tasks;
+// chunk c is visited by the 8 one-wave workgroups 8c .. 8c+7, and workgroup
+// 8c+x takes the chunk's tasks whose token t has t % 8 == x.  Each XCD so
+// reads the x rows of one eighth of the tokens, a set that stays resident
+// in its L2, while the stream order inside the chunk (group, then token)
+// is kept.  The wave's tasks are compacted into LDS; the W row of the next
+// task is in flight while the current one is reduced (two row buffers);
+// W rows are read non-temporally so they do not evict the x rows.
+constexpr int ACT_CHUNK = 128;
+constexpr int XCDS = 8;
+
 template <bool BF16, int NCH>
-__global__ __launch_bounds__(256) void expert_act(const uint16_t* __restrict__ x_,
-                                                  const uint16_t* __restrict__ W_,
-                                                  const int32_t* __restrict__ idx,
-                                                  const float* __restrict__ gate,
-                                                  const int32_t* __restrict__ perm, int M, int d,
-                                                  int K, float* __restrict__ act) {
+__global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_,
+                                                 const uint16_t* __restrict__ W_,
+                                                 const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ gate,
+                                                 const int32_t* __restrict__ perm, int M, int d,
+                                                 int K, float* __restrict__ act) {
   using V = Vec<BF16>;
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p0 = wave * ACT_TPW;
-  if (p0 >= M) return;
-  const int n = min(ACT_TPW, M - p0);
-  const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
-  const char* xb = (const char*)x_;
-  const char* Wb = (const char*)W_;
-
-  int my_m = 0, my_e = 0;
-  float my_g = 0.f;
-  if (lane < n) {
-    my_m = perm[p0 + lane];
-    my_e = idx[my_m];
-    my_g = gate[my_m];
+  __shared__ int sm[ACT_CHUNK];
+  __shared__ int se[ACT_CHUNK];
+  __shared__ float sg[ACT_CHUNK];
+  const int lane = threadIdx.x;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int chunk = blockIdx.x / XCDS, part = blockIdx.x % XCDS;
+  const int p0 = chunk * ACT_CHUNK;
+  const int n = min(ACT_CHUNK, M - p0);
+  int cnt = 0;
+  for (int h = 0; h < ACT_CHUNK; h += 64) {
+    const bool v = h + lane < n;
+    const int m = v ? perm[p0 + h + lane] : 0;
+    const bool mine = v && (m / K) % XCDS == part;
+    const unsigned long long b = __ballot(mine);
+    if (mine) {
+      const int pos = cnt + __popcll(b & lt);
+      sm[pos] = m;
+      se[pos] = idx[m];
+      sg[pos] = gate[m];
+    }
+    cnt += __popcll(b);
   }
+  if (cnt == 0) return;
+  __syncthreads();
 
-  const int cbytes = lane * 16;  // byte offset inside a 1 KB chunk
-  auto load_row = [&](const char* base, u32x4* r) {
+  // a row is NCH chunks of 64 lanes x 16 bytes; lane l holds bytes [16l, 16l+16)
+  const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
+  const unsigned cb = lane * 16u;
+  auto load_x = [&](int t, u32x4* r) {
+    const char* base = (const char*)x_ + (size_t)t * row_bytes;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const size_t o = (size_t)c * 1024 + cbytes;
+      const unsigned o = c * 1024u + cb;
       r[c] = o < row_bytes ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-
-  u32x4 xc[NCH], xn[NCH], wc[NCH], wn[NCH];
-  int t_cur = readlane(my_m, 0) / K;
-  load_row(xb + (size_t)t_cur * row_bytes, xn);
-  load_row(Wb + (size_t)readlane(my_e, 0) * row_bytes, wn);
-  for (int i = 0; i < n; ++i) {
+  auto load_w = [&](int e, u32x4* r) {
+    const char* base = (const char*)W_ + (size_t)e * row_bytes;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      xc[c] = xn[c];
-      wc[c] = wn[c];
+      const unsigned o = c * 1024u + cb;
+      r[c] = o < row_bytes ? ld16_nt(base + o) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int m = readlane(my_m, i);
-    const float g = readlane(my_g, i);
-    if (i + 1 < n) {
-      const int t_next = readlane(my_m, i + 1) / K;
-      if (t_next != t_cur) load_row(xb + (size_t)t_next * row_bytes, xn);
-      t_cur = t_next;
-      load_row(Wb + (size_t)readlane(my_e, i + 1) * row_bytes, wn);
+  };
+  u32x4 xr[NCH], wa[NCH], wb[NCH];
+  int t_cur = -1;
+  auto step = [&](int i, const u32x4* w) {
+    const int m = uni(sm[i]);
+    const float g = uni(sg[i]);
+    const int t = m / K;
+    if (t != t_cur) {  // consecutive tasks of one token reuse its x row
+      load_x(t, xr);
+      t_cur = t;
     }
-    float part = 0.f;
+    float part_sum = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) part += V::dot(xc[c], wc[c]);
-    const float h = wave_sum(part);
+    for (int c = 0; c < NCH; ++c) part_sum += V::dot(xr[c], w[c]);
+    const float h = wave_sum(part_sum);
     if (lane == 0) act[m] = g * (h / (1.f + expf(-h)));
+  };
+  load_w(uni(se[0]), wa);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) load_w(uni(se[i + 1]), wb);
+    step(i, wa);
+    if (i + 1 < cnt) {
+      if (i + 2 < cnt) load_w(uni(se[i + 2]), wa);
+      step(i + 1, wb);
+    }
   }
 }
 
-// One thread per (token, 16-byte column chunk).
+// ------------------------------------------------------------------ expert_out
+// One workgroup per token: the token's K (expert, activation) pairs are
+// staged in LDS once; each thread owns 16 bytes of y's row and streams the
+// K rows of V, OUT_UNROLL row loads in flight (kept together by a
+// scheduling barrier), then accumulates them in k order.
+constexpr int OUT_UNROLL = 16;
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void expert_out(const uint16_t* __restrict__ V_,
+__global__ __launch_bounds__(512) void expert_out(const uint16_t* __restrict__ V_,
                                                   const int32_t* __restrict__ idx,
-                                                  const float* __restrict__ act, int L, int d,
-                                                  int K, float* __restrict__ y) {
+                                                  const float* __restrict__ act, int d, int K,
+                                                  float* __restrict__ y) {
   using V = Vec<BF16>;
   constexpr int E = V::E;
-  const int upt = d / E;
-  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int t = (int)(u / upt);
-  if (t >= L) return;
-  const int c = (int)(u - (long long)t * upt) * E;
+  __shared__ int se[OMNI_MAX_K];
+  __shared__ float sa[OMNI_MAX_K];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int k = tid; k < K; k += blockDim.x) {
+    se[k] = idx[(size_t)t * K + k];
+    sa[k] = act[(size_t)t * K + k];
+  }
+  __syncthreads();
+  const int c = tid * E;
+  if (c >= d) return;
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
-  const char* Vb = (const char*)V_ + (size_t)c * (BF16 ? 2 : 4);
-  const int32_t* it = idx + (size_t)t * K;
-  const float* at = act + (size_t)t * K;
+  const unsigned cb = (unsigned)c * (BF16 ? 2u : 4u);
+  const char* Vb = (const char*)V_;
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
   int k = 0;
-  for (; k + 8 <= K; k += 8) {
-    int e[8];
-    float a[8];
-    u32x4 v[8];
+  for (; k + OUT_UNROLL <= K; k += OUT_UNROLL) {
+    u32x4 v[OUT_UNROLL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      e[j] = it[k + j];
-      a[j] = at[k + j];
-    }
+    for (int j = 0; j < OUT_UNROLL; ++j)
+      v[j] = ld16_nt(Vb + (size_t)uni(se[k + j]) * row_bytes + cb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *(const u32x4*)(Vb + (size_t)e[j] * row_bytes);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) V::axpy(a[j], v[j], acc);
+    for (int j = 0; j < OUT_UNROLL; ++j) V::axpy(uni(sa[k + j]), v[j], acc);
   }
-  for (; k < K; ++k) V::axpy(at[k], *(const u32x4*)(Vb + (size_t)it[k] * row_bytes), acc);
+  for (; k < K; ++k) V::axpy(uni(sa[k]), ld16_nt(Vb + (size_t)uni(se[k]) * row_bytes + cb), acc);
   float* yo = y + (size_t)t * d + c;
 #pragma unroll
   for (int i = 0; i < E; i += 4) *(f32x4*)(yo + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
@@ -178,10 +213,9 @@ hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const 
                         const int32_t* perm, int M, int d, int K, float* act, hipStream_t s) {
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
   const int nch = (int)((row_bytes + 1023) / 1024);
-  const int waves = (M + ACT_TPW - 1) / ACT_TPW;
-  const dim3 grid((waves + 3) / 4), block(256);
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* wp = (const uint16_t*)W;
+  const dim3 grid((unsigned)(((M + ACT_CHUNK - 1) / ACT_CHUNK) * XCDS)), block(64);
 #define OMNI_ACT(N)                                                                          \
   case N:                                                                                    \
     hipLaunchKernelGGL((expert_act<BF16, N>), grid, block, 0, s, xp, wp, idx, gate, perm, M, \
@@ -191,7 +225,7 @@ hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const 
     OMNI_ACT(1) OMNI_ACT(2) OMNI_ACT(3) OMNI_ACT(4) OMNI_ACT(5) OMNI_ACT(6) OMNI_ACT(7)
     OMNI_ACT(8)
     default:
-      return hipErrorInvalidValue;
+      return hipErrorInvalidValue;  // d above the validated limit
   }
 #undef OMNI_ACT
   return hipGetLastError();
@@ -210,14 +244,12 @@ hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, c
 hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,
                              int K, omni_dtype dt, float* y, hipStream_t s) {
   const int E = dt == OMNI_BF16 ? 8 : 4;
-  const long long units = (long long)L * (d / E);
-  const dim3 grid((unsigned)((units + 255) / 256)), block(256);
+  const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
+  const dim3 grid(L), block(threads);
   if (dt == OMNI_BF16)
-    hipLaunchKernelGGL(expert_out<true>, grid, block, 0, s, (const uint16_t*)V, idx, act, L, d, K,
-                       y);
+    hipLaunchKernelGGL(expert_out<true>, grid, block, 0, s, (const uint16_t*)V, idx, act, d, K, y);
   else
-    hipLaunchKernelGGL(expert_out<false>, grid, block, 0, s, (const uint16_t*)V, idx, act, L, d,
-                       K, y);
+    hipLaunchKernelGGL(expert_out<false>, grid, block, 0, s, (const uint16_t*)V, idx, act, d, K, y);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ struct SchedPlan {
   int M, G, ntiles, passes, digit_bits;
   size_t ws_bytes;
   // workspace carve (byte offsets)
-  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist;
+  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals;
 };
 SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,

@@ -181,50 +181,10 @@ __device__ __forceinline__ unsigned long long make_key(float v, unsigned int i) 
 __device__ __forceinline__ float key_val(unsigned long long k) { return ord_float((unsigned int)(k >> 32)); }
 __device__ __forceinline__ unsigned int key_idx(unsigned long long k) { return ~(unsigned int)k; }
 
-// One bitonic compare-exchange stage over a power-of-two array (descending).
-__device__ __forceinline__ void bitonic_stage(unsigned long long* a, int n, int k, int j) {
-  for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-    const int lo = 2 * p - (p & (j - 1));
-    const int hi = lo + j;
-    const bool desc = (lo & k) == 0;
-    const unsigned long long u = a[lo], v = a[hi];
-    if (desc ? (u < v) : (u > v)) {
-      a[lo] = v;
-      a[hi] = u;
-    }
-  }
-}
-
-// Sort two independent power-of-two arrays with shared barriers.
-__device__ void bitonic_sort2(unsigned long long* a, int na, unsigned long long* b, int nb) {
-  const int n = na > nb ? na : nb;
-  for (int k = 2; k <= n; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (k <= na) bitonic_stage(a, na, k, j);
-      if (b && k <= nb) bitonic_stage(b, nb, k, j);
-      __syncthreads();
-    }
-}
-
-__device__ float block_reduce(float v, bool is_max, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = is_max ? wave_max(v) : wave_sum(v);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  return r;
-}
-
-__host__ __device__ inline int pow2_at_least(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
+typedef unsigned long long u64;
 
 // Number of rank pairs (a, b), a < Kr, b < Kc, with (a+1)(b+1) <= K.
-__host__ __device__ inline int pair_count(int K, int Kr, int Kc) {
+inline int pair_count(int K, int Kr, int Kc) {
   int P = 0;
   for (int a = 0; a < Kr; ++a) {
     const int c = K / (a + 1);
@@ -233,94 +193,378 @@ __host__ __device__ inline int pair_count(int K, int Kr, int Kc) {
   return P;
 }
 
-__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits, int Nr,
-                                                   int Nc, int K, int nr2, int nc2, int np2,
-                                                   int32_t* __restrict__ idx,
-                                                   float* __restrict__ score,
-                                                   float* __restrict__ gate) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned long long* kr = (unsigned long long*)smem;  // [nr2] rows
-  unsigned long long* kc = kr + nr2;                    // [nc2] columns
-  unsigned long long* cand = kc + nc2;                  // [np2] candidates
-  int* off = (int*)(cand + np2);                        // [OMNI_MAX_K + 1]
-  __shared__ float red[16];
+// The top-K runs one wave (64 lanes) per token, one wave per workgroup, so
+// every synchronisation is inside a wave: no workgroup barriers gate the
+// steps.  Element i of a row / column vector lives in register v = i / 64
+// of lane i % 64.
 
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const float* sr = logits + (size_t)t * (Nr + Nc);
-  const float* sc = sr + Nr;
+// Digit search of one radix pass: hist[0..256) counts the keys that match
+// the current prefix by their digit.  Returns the largest digit d whose
+// suffix count sum_{d' >= d} hist[d'] reaches `need`, with that bucket's
+// size (*hd) and the count strictly above it (*above).  Lane l reads bins
+// 4l .. 4l+3.
+__device__ __forceinline__ int find_digit(const int* hist, int need, int* hd, int* above) {
+  const int lane = threadIdx.x & 63;
+  const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+  const int h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const int sl = h0 + h1 + h2 + h3;
+  int incl = sl;  // inclusive suffix sum over lanes lane..63
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += v;
+  }
+  const int s3 = incl - sl + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+  int best = -1;
+  if (s0 >= need) best = 4 * lane;
+  if (s1 >= need) best = 4 * lane + 1;
+  if (s2 >= need) best = 4 * lane + 2;
+  if (s3 >= need) best = 4 * lane + 3;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+  const int q = best & 3;
+  const int hq = q == 0 ? h0 : q == 1 ? h1 : q == 2 ? h2 : h3;
+  const int sq = q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3;
+  *hd = __shfl(hq, best >> 2, 64);
+  *above = __shfl(sq, best >> 2, 64) - *hd;
+  return best;
+}
 
-  // LogSoftmax: p = s - (max + log sum exp(s - max)), rows and columns.
-  float mr = -INFINITY, mc = -INFINITY;
-  for (int i = tid; i < Nr; i += blockDim.x) mr = fmaxf(mr, sr[i]);
-  for (int j = tid; j < Nc; j += blockDim.x) mc = fmaxf(mc, sc[j]);
-  mr = block_reduce(mr, true, red);
-  mc = block_reduce(mc, true, red + 8);
-  float er = 0.f, ec = 0.f;
-  for (int i = tid; i < Nr; i += blockDim.x) er += expf(sr[i] - mr);
-  for (int j = tid; j < Nc; j += blockDim.x) ec += expf(sc[j] - mc);
-  er = block_reduce(er, false, red);
-  ec = block_reduce(ec, false, red + 8);
-  const float lse_r = mr + logf(er), lse_c = mc + logf(ec);
+__device__ __forceinline__ void zero_hist(int* hist) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+}
 
-  for (int i = tid; i < nr2; i += blockDim.x) kr[i] = i < Nr ? make_key(sr[i] - lse_r, i) : 0ull;
-  for (int j = tid; j < nc2; j += blockDim.x) kc[j] = j < Nc ? make_key(sc[j] - lse_c, j) : 0ull;
-  __syncthreads();
-  bitonic_sort2(kr, nr2, kc, nc2);
+__device__ __forceinline__ unsigned wave_umax(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_umin(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
 
-  // Candidate rank pairs: row rank a keeps the first min(Kc, K/(a+1)) columns.
-  const int Kr = K < Nr ? K : Nr, Kc = K < Nc ? K : Nc;
-  if (tid < 64) {
-    // wave 0: exclusive scan of the per-row counts (Kr <= 512 -> 8 per lane)
-    const int per = (Kr + 63) / 64;
-    const int a0 = tid * per;
-    int loc = 0;
-    for (int a = a0; a < a0 + per && a < Kr; ++a) {
-      const int c = K / (a + 1);
-      loc += c < Kc ? c : Kc;
+// Select the R largest of n register-resident values under (value desc,
+// index asc); val[v] holds element v*64 + lane.  Radix select over the
+// 32-bit value (8-bit digits, starting at the first byte where the values
+// differ, stopping once the boundary bucket is exactly what is still
+// needed); value ties at the threshold are broken by smallest index.  The R
+// keys are written to out[0..R) in index order.
+template <int VPL>
+__device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, int* hist, u64* out) {
+  const int lane = threadIdx.x & 63;
+  const u64 lt = (1ull << lane) - 1ull;
+  unsigned prefix = 0, pmask = 0;
+  int need = R;
+  bool done = R >= n;
+  if (!done) {
+    unsigned mx = 0, mn = 0xffffffffu;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (v * 64 + lane < n) {
+        mx = max(mx, val[v]);
+        mn = min(mn, val[v]);
+      }
+    mx = wave_umax(mx);
+    mn = wave_umin(mn);
+    const unsigned diff = mx ^ mn;
+    int pass0 = diff ? __clz(diff) / 8 : 3;  // leading bytes shared by all values
+    pmask = pass0 ? 0xffffffffu << (32 - 8 * pass0) : 0u;
+    prefix = mx & pmask;
+    for (int pass = pass0; pass < 4 && !done; ++pass) {
+      const int shift = 24 - 8 * pass;
+      zero_hist(hist);
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (v * 64 + lane < n && (val[v] & pmask) == prefix)
+          atomicAdd(&hist[(val[v] >> shift) & 255], 1);
+      __syncthreads();
+      int hd, above;
+      const int dig = find_digit(hist, need, &hd, &above);
+      __syncthreads();
+      prefix |= (unsigned)dig << shift;
+      pmask |= 0xffu << shift;
+      need -= above;
+      done = hd == need || shift == 0;
     }
+  }
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int i = v * 64 + lane;
+    const bool valid = i < n;
+    const unsigned m = val[v] & pmask;
+    const bool eq = valid && m == prefix;
+    const u64 be = __ballot(eq);
+    const bool sel = (valid && m > prefix) || (eq && ties + __popcll(be & lt) < need);
+    ties += __popcll(be);
+    const u64 bs = __ballot(sel);
+    const int pos = base + __popcll(bs & lt);
+    if (sel && pos < R) out[pos] = ((u64)val[v] << 32) | (u64)(~(unsigned)i);
+    base += __popcll(bs);
+  }
+}
+
+// Select the R largest of n unique 64-bit keys in LDS; the R keys are
+// written to out[0..R) in input order.
+__device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* out) {
+  const int lane = threadIdx.x & 63;
+  const u64 lt = (1ull << lane) - 1ull;
+  u64 prefix = 0, pmask = 0;
+  int need = R;
+  bool done = R >= n;
+  if (!done) {
+    unsigned mx = 0, mn = 0xffffffffu;  // range of the high (score) word
+    for (int i = lane; i < n; i += 64) {
+      const unsigned h = (unsigned)(keys[i] >> 32);
+      mx = max(mx, h);
+      mn = min(mn, h);
+    }
+    mx = wave_umax(mx);
+    mn = wave_umin(mn);
+    const unsigned diff = mx ^ mn;
+    const int pass0 = diff ? __clz(diff) / 8 : 4;
+    pmask = pass0 ? ~0ull << (64 - 8 * pass0) : 0ull;
+    prefix = ((u64)mx << 32) & pmask;
+    for (int pass = pass0; pass < 8 && !done; ++pass) {
+      const int shift = 56 - 8 * pass;
+      zero_hist(hist);
+      __syncthreads();
+      for (int i = lane; i < n; i += 64) {
+        const u64 k = keys[i];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255)], 1);
+      }
+      __syncthreads();
+      int hd, above;
+      const int dig = find_digit(hist, need, &hd, &above);
+      __syncthreads();
+      prefix |= (u64)dig << shift;
+      pmask |= 0xffull << shift;
+      need -= above;
+      done = hd == need || shift == 0;
+    }
+  }
+  int base = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const u64 k = i < n ? keys[i] : 0ull;
+    const bool sel = i < n && (k & pmask) >= prefix;
+    const u64 bs = __ballot(sel);
+    const int pos = base + __popcll(bs & lt);
+    if (sel && pos < R) out[pos] = k;  // exactly R keys qualify
+    base += __popcll(bs);
+  }
+}
+
+// Bitonic sort (descending) of 64*V keys held by one wave: element
+// e = v*64 + lane lives in register k[v] of lane `lane`.
+template <int V>
+__device__ void wave_sort_desc(u64 (&k)[V]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * V; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int jr = j >> 6;  // partner register
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          if (v & jr) continue;
+          const bool desc = (((v * 64 + lane) & size) == 0);
+          const u64 a = k[v], b = k[v | jr];
+          const bool sw = desc ? (a < b) : (a > b);
+          k[v] = sw ? b : a;
+          k[v | jr] = sw ? a : b;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const bool desc = (((v * 64 + lane) & size) == 0);
+          const u64 o = __shfl_xor(k[v], j, 64);
+          const bool lower = (lane & j) == 0;
+          const bool keep_max = lower == desc;
+          k[v] = keep_max ? (k[v] > o ? k[v] : o) : (k[v] < o ? k[v] : o);
+        }
+      }
+    }
+  }
+}
+
+// Sort arr[0..n) (n <= 512) in place, descending.
+template <int V>
+__device__ void wave_sort_lds_t(u64* arr, int n) {
+  const int lane = threadIdx.x & 63;
+  u64 k[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) k[v] = v * 64 + lane < n ? arr[v * 64 + lane] : 0ull;
+  wave_sort_desc<V>(k);
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (v * 64 + lane < n) arr[v * 64 + lane] = k[v];
+}
+
+__device__ void wave_sort_lds(u64* arr, int n) {
+  if (n <= 64) wave_sort_lds_t<1>(arr, n);
+  else if (n <= 128) wave_sort_lds_t<2>(arr, n);
+  else if (n <= 256) wave_sort_lds_t<4>(arr, n);
+  else wave_sort_lds_t<8>(arr, n);
+}
+
+// Order the K selected candidates, softmax gate, write the token's outputs.
+template <int V>
+__device__ void emit_topk(const u64* fs, int K, int32_t* idx, float* score, float* gate) {
+  const int lane = threadIdx.x & 63;
+  u64 k[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) k[v] = v * 64 + lane < K ? fs[v * 64 + lane] : 0ull;
+  wave_sort_desc<V>(k);
+  const float s0 = key_val(__shfl(k[0], 0, 64));  // largest score
+  float es = 0.f;
+  float ev[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    ev[v] = v * 64 + lane < K ? expf(key_val(k[v]) - s0) : 0.f;
+    es += ev[v];
+  }
+  const float inv = 1.f / wave_sum(es);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = v * 64 + lane;
+    if (e < K) {
+      idx[e] = (int32_t)key_idx(k[v]);
+      score[e] = key_val(k[v]);
+      gate[e] = ev[v] * inv;
+    }
+  }
+}
+
+struct TopkLayout {
+  int Kr, Kc, P;
+  size_t o_rs, o_cs, o_cand, o_fs, o_hist, o_off, bytes;
+};
+
+inline TopkLayout topk_layout(int Nr, int Nc, int K) {
+  TopkLayout l;
+  l.Kr = K < Nr ? K : Nr;
+  l.Kc = K < Nc ? K : Nc;
+  l.P = pair_count(K, l.Kr, l.Kc);
+  size_t o = 0;
+  l.o_rs = o; o += (size_t)l.Kr * 8;
+  l.o_cs = o; o += (size_t)l.Kc * 8;
+  l.o_cand = o; o += (size_t)l.P * 8;
+  l.o_fs = o; o += (size_t)K * 8;
+  l.o_hist = o; o += 256 * 4;
+  l.o_off = o; o += (size_t)(l.Kr + 1) * 4;
+  l.bytes = o;
+  return l;
+}
+
+// Load one logit vector (n <= 64*VPL) and turn it into LogSoftmax values,
+// p = s - (max + log sum exp(s - max)), kept as order-preserving words.
+template <int VPL>
+__device__ __forceinline__ void log_softmax_ord(const float* s, int n, unsigned (&val)[VPL]) {
+  const int lane = threadIdx.x & 63;
+  float f[VPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    f[v] = v * 64 + lane < n ? s[v * 64 + lane] : -INFINITY;
+    m = fmaxf(m, f[v]);
+  }
+  m = wave_max(m);
+  float e = 0.f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) e += v * 64 + lane < n ? expf(f[v] - m) : 0.f;
+  const float lse = m + logf(wave_sum(e));
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) val[v] = v * 64 + lane < n ? float_ord(f[v] - lse) : 0u;
+}
+
+// One wave per token.
+//  1. LogSoftmax of the row and column logits.
+//  2. Row pre-selection: the first min(K, N_r) rows under (p_r desc, i asc);
+//     columns likewise.  A cell outside these rows or columns has at least
+//     K cells before it under (S desc, n asc), so the top K lies inside.
+//  3. Candidates: row rank a (0-based) is paired with the first
+//     min(K_c, K/(a+1)) columns: a cell at ranks (a, b) has at least
+//     (a+1)(b+1) - 1 cells before it, so (a+1)(b+1) <= K is necessary.
+//  4. Top K of the candidates under (S desc, n asc); gate = softmax of S.
+template <int VPL>
+__global__ __launch_bounds__(64) void router_topk(const float* __restrict__ logits, int Nr, int Nc,
+                                                  int K, const TopkLayout lay,
+                                                  int32_t* __restrict__ idx,
+                                                  float* __restrict__ score,
+                                                  float* __restrict__ gate) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u64* rs = (u64*)(smem + lay.o_rs);
+  u64* cs = (u64*)(smem + lay.o_cs);
+  u64* cand = (u64*)(smem + lay.o_cand);
+  u64* fs = (u64*)(smem + lay.o_fs);
+  int* hist = (int*)(smem + lay.o_hist);
+  int* off = (int*)(smem + lay.o_off);
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float* sr = logits + (size_t)t * (Nr + Nc);
+
+  // 1-2. rows, then columns
+  {
+    unsigned val[VPL];
+    log_softmax_ord<VPL>(sr, Nr, val);
+    select_top_regs<VPL>(val, Nr, lay.Kr, hist, rs);
+    log_softmax_ord<VPL>(sr + Nr, Nc, val);
+    __syncthreads();
+    select_top_regs<VPL>(val, Nc, lay.Kc, hist, cs);
+  }
+  __syncthreads();
+  wave_sort_lds(rs, lay.Kr);
+  wave_sort_lds(cs, lay.Kc);
+  {
+    // exclusive scan of the per-row candidate counts (K_r <= 512)
+    const int per = (lay.Kr + 63) / 64;
+    const int a0 = lane * per;
+    int loc = 0;
+    for (int a = a0; a < a0 + per && a < lay.Kr; ++a) loc += min(lay.Kc, K / (a + 1));
     int inc = loc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(inc, o, 64);
-      if (tid >= o) inc += v;
+      if (lane >= o) inc += v;
     }
     int run = inc - loc;
-    for (int a = a0; a < a0 + per && a < Kr; ++a) {
+    for (int a = a0; a < a0 + per && a < lay.Kr; ++a) {
       off[a] = run;
-      const int c = K / (a + 1);
-      run += c < Kc ? c : Kc;
+      run += min(lay.Kc, K / (a + 1));
     }
-    if (tid == 63) off[Kr] = inc;
+    if (lane == 63) off[lay.Kr] = inc;
   }
   __syncthreads();
-  const int P = off[Kr];
-  for (int a = tid; a < Kr; a += blockDim.x) {
-    const unsigned long long rk = kr[a];
-    const float pr = key_val(rk);
-    const unsigned int i = key_idx(rk);
-    const int base = off[a], cnt = off[a + 1] - base;
-    for (int b = 0; b < cnt; ++b) {
-      const unsigned long long ck = kc[b];
-      cand[base + b] = make_key(pr + key_val(ck), i * (unsigned int)Nc + key_idx(ck));
-    }
-  }
-  for (int c = P + tid; c < np2; c += blockDim.x) cand[c] = 0ull;
-  __syncthreads();
-  bitonic_sort2(cand, np2, nullptr, 0);
 
-  // Gate: softmax over the K selected scores (cand[0] holds the largest).
-  const float s0 = key_val(cand[0]);
-  float es = 0.f;
-  for (int k = tid; k < K; k += blockDim.x) es += expf(key_val(cand[k]) - s0);
-  es = block_reduce(es, false, red);
-  const float inv = 1.f / es;
-  for (int k = tid; k < K; k += blockDim.x) {
-    const unsigned long long ck = cand[k];
-    const float s = key_val(ck);
-    idx[(size_t)t * K + k] = (int32_t)key_idx(ck);
-    score[(size_t)t * K + k] = s;
-    gate[(size_t)t * K + k] = expf(s - s0) * inv;
+  // 3. candidate c belongs to the row rank a with off[a] <= c < off[a+1]
+  for (int c = lane; c < lay.P; c += 64) {
+    int lo = 0, hi = lay.Kr - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    const u64 rk = rs[lo], ck = cs[c - off[lo]];
+    cand[c] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
   }
+  __syncthreads();
+
+  // 4. top K of the candidates, ordered, gated and written
+  select_top_lds(cand, lay.P, K, hist, fs);
+  __syncthreads();
+  int32_t* io = idx + (size_t)t * K;
+  float* so = score + (size_t)t * K;
+  float* go = gate + (size_t)t * K;
+  if (K <= 64) emit_topk<1>(fs, K, io, so, go);
+  else if (K <= 128) emit_topk<2>(fs, K, io, so, go);
+  else if (K <= 256) emit_topk<4>(fs, K, io, so, go);
+  else emit_topk<8>(fs, K, io, so, go);
 }
 
 }  // namespace
@@ -340,27 +584,24 @@ hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int
   return hipGetLastError();
 }
 
-size_t router_topk_lds_bytes(int Nr, int Nc, int K) {
-  const int Kr = K < Nr ? K : Nr, Kc = K < Nc ? K : Nc;
-  const int np2 = pow2_at_least(pair_count(K, Kr, Kc));
-  return (size_t)(pow2_at_least(Nr) + pow2_at_least(Nc) + np2) * 8 + (OMNI_MAX_K + 1) * 4;
-}
+size_t router_topk_lds_bytes(int Nr, int Nc, int K) { return topk_layout(Nr, Nc, K).bytes; }
 
 hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K, int32_t* idx,
                               float* score, float* gate, hipStream_t s) {
-  const int Kr = K < Nr ? K : Nr, Kc = K < Nc ? K : Nc;
-  const int nr2 = pow2_at_least(Nr), nc2 = pow2_at_least(Nc);
-  const int np2 = pow2_at_least(pair_count(K, Kr, Kc));
-  const size_t lds = router_topk_lds_bytes(Nr, Nc, K);
-  if (lds > 64 * 1024) {
-    // beyond the default 64 KB of dynamic LDS: ask for exactly what is needed
-    hipError_t e = hipFuncSetAttribute((const void*)router_topk,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  const TopkLayout lay = topk_layout(Nr, Nc, K);
+  const int need = (max(Nr, Nc) + 63) / 64;  // values per lane
+  // at most K*(2 + H(K)) + K keys: under 40 KB for K <= 512
+  const size_t lds = lay.bytes;
+#define OMNI_TOPK(V)                                                                           \
+  if (need <= V) {                                                                             \
+    hipLaunchKernelGGL(router_topk<V>, dim3(L), dim3(64), lds, s, logits, Nr, Nc, K, lay, idx, \
+                       score, gate);                                                           \
+    return hipGetLastError();                                                                  \
   }
-  hipLaunchKernelGGL(router_topk, dim3(L), dim3(256), lds, s, logits, Nr, Nc, K, nr2, nc2, np2,
-                     idx, score, gate);
-  return hipGetLastError();
+  OMNI_TOPK(1) OMNI_TOPK(2) OMNI_TOPK(4) OMNI_TOPK(8) OMNI_TOPK(12) OMNI_TOPK(16) OMNI_TOPK(24)
+  OMNI_TOPK(32) OMNI_TOPK(48) OMNI_TOPK(64)
+#undef OMNI_TOPK
+  return hipErrorInvalidValue;  // N_r, N_c above 4096 are rejected before launch
 }
 
 }  // namespace omni

@@ -10,7 +10,7 @@
 // therefore yields the order (group, token, m): the key needs only
 // ceil(log2 G) bits.  It is an LSD radix sort with up to 8-bit digits:
 //   sched_hist     per-tile digit histograms (digit-major table)
-//   sched_scan     exclusive scan of that table (one workgroup)
+//   sched_scan_digits  per digit: exclusive scan over tiles, digit total
 //   sched_scatter  stable scatter: in-tile ranks from wave ballots
 // followed by sched_offsets, which turns the sorted group ids into
 // group_off[q] = first sorted position whose group is >= q.
@@ -46,44 +46,85 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __res
   if (tid < radix) hist[tid * ntiles + tile] = h[tid];
 }
 
-// Exclusive scan of n ints in place by one 1024-thread workgroup.
-__global__ __launch_bounds__(1024) void sched_scan(int* __restrict__ a, int n) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int lo = tid * per, hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += a[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-    const int v = tid >= o ? part[tid - o] : 0;
+// Row d of the digit-major table holds digit d's count in every tile.  One
+// workgroup per digit turns its row into an exclusive scan over tiles and
+// stores the digit's total.
+__global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(int* __restrict__ hist,
+                                                                   int ntiles,
+                                                                   int* __restrict__ totals) {
+  __shared__ int wsum[SCHED_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* row = hist + (size_t)blockIdx.x * ntiles;
+  int carry = 0;
+  for (int base = 0; base < ntiles; base += SCHED_THREADS * 4) {
+    const int i0 = base + tid * 4;
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = i0 + q < ntiles ? row[i0 + q] : 0;
+    const int s = v[0] + v[1] + v[2] + v[3];
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
-    part[tid] += v;
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < SCHED_THREADS / 64; ++w) {
+      woff += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    int run = carry + woff + inc - s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q < ntiles) row[i0 + q] = run;
+      run += v[q];
+    }
+    carry += tot;
     __syncthreads();
   }
-  int run = part[tid] - s;
-  for (int i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
+  if (tid == 0) totals[blockIdx.x] = carry;
 }
 
 __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
     const int32_t* __restrict__ vals_in, int M, int B, int shift, int radix, int ntiles,
-    const int* __restrict__ hist, int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+    const int* __restrict__ hist, const int* __restrict__ totals, int32_t* __restrict__ keys_out,
+    int32_t* __restrict__ vals_out) {
   __shared__ int run[256];
   __shared__ int wcnt[SCHED_THREADS / 64][256];
   const int tid = threadIdx.x, tile = blockIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int dbits = 31 - __clz(radix);
+  if (wave == 0) {
+    // exclusive scan of the digit totals (radix <= 256: 4 per lane)
+    int v[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = 4 * lane + q < radix ? totals[4 * lane + q] : 0;
+      s += v[q];
+    }
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    int b = inc - s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (4 * lane + q < radix) run[4 * lane + q] = b;
+      b += v[q];
+    }
+  }
   if (tid < radix) {
-    run[tid] = hist[tid * ntiles + tile];
 #pragma unroll
     for (int w = 0; w < SCHED_THREADS / 64; ++w) wcnt[w][tid] = 0;
   }
+  __syncthreads();
+  if (tid < radix) run[tid] += hist[(size_t)tid * ntiles + tile];
   __syncthreads();
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int base = tile * SCHED_TILE;
@@ -156,7 +197,8 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B) {
   p.off_keys_b = 2 * arr;
   p.off_vals_b = 3 * arr;
   p.off_hist = 4 * arr;
-  p.ws_bytes = p.off_hist + align256((size_t)(1 << p.digit_bits) * p.ntiles * 4);
+  p.off_totals = p.off_hist + align256((size_t)(1 << p.digit_bits) * p.ntiles * 4);
+  p.ws_bytes = p.off_totals + align256(256 * 4);
   return p;
 }
 
@@ -168,6 +210,7 @@ hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedP
   int32_t* kb = (int32_t*)(w + plan.off_keys_b);
   int32_t* vb = (int32_t*)(w + plan.off_vals_b);
   int* hist = (int*)(w + plan.off_hist);
+  int* totals = (int*)(w + plan.off_totals);
   const int radix = 1 << plan.digit_bits;
   const int32_t* kin = nullptr;  // pass 0 derives keys from idx
   const int32_t* vin = nullptr;  // pass 0 values are the task ids
@@ -178,9 +221,10 @@ hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedP
     const int shift = pass * plan.digit_bits;
     hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M, B,
                        shift, radix, plan.ntiles, hist);
-    hipLaunchKernelGGL(sched_scan, dim3(1), dim3(1024), 0, s, hist, radix * plan.ntiles);
+    hipLaunchKernelGGL(sched_scan_digits, dim3(radix), dim3(SCHED_THREADS), 0, s, hist,
+                       plan.ntiles, totals);
     hipLaunchKernelGGL(sched_scatter, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, vin,
-                       M, B, shift, radix, plan.ntiles, hist, kout, vout);
+                       M, B, shift, radix, plan.ntiles, hist, totals, kout, vout);
     kin = kout;
     vin = vout;
   }

@@ -45,13 +45,39 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
+                    help="tokens the CPU oracle routes and assembles (capped at L)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB "
+                         "(reference kernel for scaling hardware byte counters)")
     return ap.parse_args()
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+ASSEMBLY_SRC = os.path.join(ROOT, "atomic_expert_routing_amd", "csrc", "assembly.hip")
+PROFILE = os.path.join(ROOT, "profiles", "routed_forward_L4096_N1700416_d2048.md")
+
+
+def measured_traffic(workload_name):
+    """Counter-measured bytes per assembly call from the committed rocprofv3
+    summary, or None when it was taken on other kernel source or workload."""
+    import hashlib
+    import re
+
+    if workload_name != "L4096_N1700416_d2048" or not os.path.exists(PROFILE):
+        return None
+    text = open(PROFILE).read()
+    m_hash = re.search(r"assembly\.hip sha256: ([0-9a-f]{64})", text)
+    m_bytes = re.search(r"assembly call traffic bytes: (\d+)", text)
+    if not (m_hash and m_bytes):
+        return None
+    if hashlib.sha256(open(ASSEMBLY_SRC, "rb").read()).hexdigest() != m_hash.group(1):
+        return None
+    return int(m_bytes.group(1))
 
 
 def cpu_baseline(inp, w, n_tok, seed):
@@ -98,7 +124,8 @@ def cpu_baseline(inp, w, n_tok, seed):
         "kind": "oracle",
         "sample": (f"{len(toks)} of {w.L} tokens (seeded), router+schedule+expert-centric "
                    f"assembly in float64, {secs:.2f} s measured, scaled x{w.L / len(toks):g}; "
-                   f"host affinity {len(os.sched_getaffinity(0))} cpus"),
+                   f"host affinity {len(os.sched_getaffinity(0))} cpus; W/V rows and router "
+                   f"weights copied to host before timing"),
         "stages_s": {"route": round(t_route, 3), "schedule+assembly": round(t_rest, 3)},
     }
 
@@ -135,6 +162,16 @@ def main():
         br.expert_forward(inp["x"], inp["W"], inp["V"])
         if ev is not None:
             ev[3].record()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + written")
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -195,7 +232,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "algorithmic_bytes": expert_bytes,
             "mean_ms": round(expert_mean_ms, 4),
         },

@@ -136,7 +136,7 @@ OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
  * reused by its tokens); the output pass sums each token's K terms in k
  * order without atomics, so y is deterministic.
  * Requires d % 8 == 0, d <= OMNI_MAX_D_BF16 (bf16) or OMNI_MAX_D_F32 (fp32),
- * L*K < 2^31, N < 2^31.  Workspace: fp32 activations [L*K].
+ * K <= OMNI_MAX_K, L*K < 2^31, N < 2^31.  Workspace: fp32 activations [L*K].
  */
 OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const void* V,
                                 const int32_t* idx, const float* gate,

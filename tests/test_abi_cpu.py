@@ -86,6 +86,12 @@ def test_fp32_d_limit_is_lower():
     assert e.value.status == omni.OMNI_ERR_UNSUPPORTED
 
 
+def test_expert_forward_k_limit():
+    with pytest.raises(omni.OmniError) as e:
+        omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4, d=64, K=513, N=10000)
+    assert e.value.status == omni.OMNI_ERR_UNSUPPORTED
+
+
 def test_schedule_validation():
     for kw in (dict(N=0), dict(B=0), dict(N=2**31)):
         args = dict(L=4, K=2, N=100, B=8)

@@ -79,6 +79,8 @@ RAGGED = [
     (64, 64, 32, 32, 16, 5000, "bf16"),   # B >= N: one group
     (40, 64, 600, 700, 512, 512, "bf16"),  # K at its limit
     (20, 64, 4096, 3, 100, 33, "f32"),    # grid side at its limit
+    (33, 64, 2900, 70, 256, 64, "bf16"),  # 46 row values per lane
+    (17, 48, 700, 1100, 200, 77, "bf16"),  # 11 and 18 values per lane
     (16, 4096, 64, 64, 32, 64, "bf16"),   # d at its bf16 limit
     (24, 2048, 40, 40, 20, 16, "f32"),    # d at its fp32 limit
 ]
