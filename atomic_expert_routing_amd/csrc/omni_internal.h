@@ -25,15 +25,81 @@ __device__ __forceinline__ void widen8(const u32x4 v, float* f) {
   f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// ----------------------------------------------------------------- wave exchanges
+// DPP (data-parallel primitives) move a value between lanes inside the VALU
+// instead of through the LDS crossbar.  gfx9 encodings:
+//   quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2)
+//   row_shl:n = 0x100+n (lane i reads i+n in its row of 16), row_shr:n = 0x110+n
+//   row_ror:n = 0x120+n, row_mirror = 0x140, row_half_mirror = 0x141
+//   row_bcast:15 = 0x142, row_bcast:31 = 0x143
+template <int CTRL, int ROWS = 0xf, bool ZERO_OOB = false>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, ZERO_OOB);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Value held by lane ^ J (J a power of two below 64).
+template <int J>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (J == 1) {
+    return dpp<0xB1>(v);
+  } else if constexpr (J == 2) {
+    return dpp<0x4E>(v);
+  } else if constexpr (J == 4 || J == 8) {
+    const int from_below = dpp<0x110 + J>(v);  // lane i reads i - J
+    const int from_above = dpp<0x100 + J>(v);  // lane i reads i + J
+    return (threadIdx.x & J) ? from_below : from_above;
+  } else if constexpr (J == 16) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);  // bit mode: xor 16 within 32 lanes
+  } else {
+    return __shfl_xor(v, J, 64);
+  }
+}
+
+__device__ __forceinline__ float fxor_lane1(float v) { return __int_as_float(dpp<0xB1>(__float_as_int(v))); }
+
+// Reductions: xor 1 and xor 2 inside quads, then half-row and row mirrors
+// leave every lane of a 16-lane row holding the row's result; the four rows
+// are combined through scalar reads (so the result is wave-uniform).
+#define OMNI_ROW_REDUCE(T, AS, FROM, OP)                        \
+  v = OP(v, FROM(dpp<0xB1>(AS(v))));                            \
+  v = OP(v, FROM(dpp<0x4E>(AS(v))));                            \
+  v = OP(v, FROM(dpp<0x141>(AS(v))));                           \
+  v = OP(v, FROM(dpp<0x140>(AS(v))));                           \
+  const T r0 = FROM(__builtin_amdgcn_readlane(AS(v), 0));       \
+  const T r1 = FROM(__builtin_amdgcn_readlane(AS(v), 16));      \
+  const T r2 = FROM(__builtin_amdgcn_readlane(AS(v), 32));      \
+  const T r3 = FROM(__builtin_amdgcn_readlane(AS(v), 48));      \
+  return OP(OP(OP(r0, r1), r2), r3);
+
+__device__ __forceinline__ float add_f(float a, float b) { return a + b; }
+__device__ __forceinline__ int add_i(int a, int b) { return a + b; }
+__device__ __forceinline__ int max_i(int a, int b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned max_u(unsigned a, unsigned b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned min_u(unsigned a, unsigned b) { return a < b ? a : b; }
+__device__ __forceinline__ int f2i(float f) { return __float_as_int(f); }
+__device__ __forceinline__ float i2f(int i) { return __int_as_float(i); }
+__device__ __forceinline__ int u2i(unsigned u) { return (int)u; }
+__device__ __forceinline__ unsigned i2u(int i) { return (unsigned)i; }
+__device__ __forceinline__ int id_i(int i) { return i; }
+
+__device__ __forceinline__ float wave_sum(float v) { OMNI_ROW_REDUCE(float, f2i, i2f, add_f) }
+__device__ __forceinline__ float wave_max(float v) { OMNI_ROW_REDUCE(float, f2i, i2f, fmaxf) }
+__device__ __forceinline__ int wave_max_i(int v) { OMNI_ROW_REDUCE(int, id_i, id_i, max_i) }
+__device__ __forceinline__ int wave_sum_i(int v) { OMNI_ROW_REDUCE(int, id_i, id_i, add_i) }
+__device__ __forceinline__ unsigned wave_umax(unsigned v) { OMNI_ROW_REDUCE(unsigned, u2i, i2u, max_u) }
+__device__ __forceinline__ unsigned wave_umin(unsigned v) { OMNI_ROW_REDUCE(unsigned, u2i, i2u, min_u) }
+#undef OMNI_ROW_REDUCE
+
+// Inclusive prefix sum over the 64 lanes: row_shr steps inside each row of
+// 16 (lanes below the shift add 0), then row broadcasts of lane 15 into
+// rows 1 and 3 and of lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp<0x111, 0xf, true>(v);
+  v += dpp<0x112, 0xf, true>(v);
+  v += dpp<0x114, 0xf, true>(v);
+  v += dpp<0x118, 0xf, true>(v);
+  v += dpp<0x142, 0xa>(v);
+  v += dpp<0x143, 0xc>(v);
   return v;
 }
 

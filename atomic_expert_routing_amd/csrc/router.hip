@@ -198,6 +198,14 @@ inline int pair_count(int K, int Kr, int Kc) {
 // steps.  Element i of a row / column vector lives in register v = i / 64
 // of lane i % 64.
 
+// Orders this wave's LDS accesses: the wave works alone on its token, so a
+// workgroup barrier is not needed (and several tokens share a workgroup).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Digit search of one radix pass: hist[0..256) counts the keys that match
 // the current prefix by their digit.  Returns the largest digit d whose
 // suffix count sum_{d' >= d} hist[d'] reaches `need`, with that bucket's
@@ -208,20 +216,15 @@ __device__ __forceinline__ int find_digit(const int* hist, int need, int* hd, in
   const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
   const int h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
   const int sl = h0 + h1 + h2 + h3;
-  int incl = sl;  // inclusive suffix sum over lanes lane..63
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_down(incl, o, 64);
-    if (lane + o < 64) incl += v;
-  }
+  const int pre = wave_incl_scan(sl);                              // lanes 0..lane
+  const int incl = __builtin_amdgcn_readlane(pre, 63) - pre + sl;  // lanes lane..63
   const int s3 = incl - sl + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
   int best = -1;
   if (s0 >= need) best = 4 * lane;
   if (s1 >= need) best = 4 * lane + 1;
   if (s2 >= need) best = 4 * lane + 2;
   if (s3 >= need) best = 4 * lane + 3;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+  best = wave_max_i(best);
   const int q = best & 3;
   const int hq = q == 0 ? h0 : q == 1 ? h1 : q == 2 ? h2 : h3;
   const int sq = q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3;
@@ -234,79 +237,6 @@ __device__ __forceinline__ void zero_hist(int* hist) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
-}
-
-__device__ __forceinline__ unsigned wave_umax(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
-  return v;
-}
-__device__ __forceinline__ unsigned wave_umin(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o, 64));
-  return v;
-}
-
-// Select the R largest of n register-resident values under (value desc,
-// index asc); val[v] holds element v*64 + lane.  Radix select over the
-// 32-bit value (8-bit digits, starting at the first byte where the values
-// differ, stopping once the boundary bucket is exactly what is still
-// needed); value ties at the threshold are broken by smallest index.  The R
-// keys are written to out[0..R) in index order.
-template <int VPL>
-__device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, int* hist, u64* out) {
-  const int lane = threadIdx.x & 63;
-  const u64 lt = (1ull << lane) - 1ull;
-  unsigned prefix = 0, pmask = 0;
-  int need = R;
-  bool done = R >= n;
-  if (!done) {
-    unsigned mx = 0, mn = 0xffffffffu;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (v * 64 + lane < n) {
-        mx = max(mx, val[v]);
-        mn = min(mn, val[v]);
-      }
-    mx = wave_umax(mx);
-    mn = wave_umin(mn);
-    const unsigned diff = mx ^ mn;
-    int pass0 = diff ? __clz(diff) / 8 : 3;  // leading bytes shared by all values
-    pmask = pass0 ? 0xffffffffu << (32 - 8 * pass0) : 0u;
-    prefix = mx & pmask;
-    for (int pass = pass0; pass < 4 && !done; ++pass) {
-      const int shift = 24 - 8 * pass;
-      zero_hist(hist);
-      __syncthreads();
-#pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (v * 64 + lane < n && (val[v] & pmask) == prefix)
-          atomicAdd(&hist[(val[v] >> shift) & 255], 1);
-      __syncthreads();
-      int hd, above;
-      const int dig = find_digit(hist, need, &hd, &above);
-      __syncthreads();
-      prefix |= (unsigned)dig << shift;
-      pmask |= 0xffu << shift;
-      need -= above;
-      done = hd == need || shift == 0;
-    }
-  }
-  int base = 0, ties = 0;
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int i = v * 64 + lane;
-    const bool valid = i < n;
-    const unsigned m = val[v] & pmask;
-    const bool eq = valid && m == prefix;
-    const u64 be = __ballot(eq);
-    const bool sel = (valid && m > prefix) || (eq && ties + __popcll(be & lt) < need);
-    ties += __popcll(be);
-    const u64 bs = __ballot(sel);
-    const int pos = base + __popcll(bs & lt);
-    if (sel && pos < R) out[pos] = ((u64)val[v] << 32) | (u64)(~(unsigned)i);
-    base += __popcll(bs);
-  }
 }
 
 // Select the R largest of n unique 64-bit keys in LDS; the R keys are
@@ -333,15 +263,15 @@ __device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* ou
     for (int pass = pass0; pass < 8 && !done; ++pass) {
       const int shift = 56 - 8 * pass;
       zero_hist(hist);
-      __syncthreads();
+      wave_sync();
       for (int i = lane; i < n; i += 64) {
         const u64 k = keys[i];
         if ((k & pmask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255)], 1);
       }
-      __syncthreads();
+      wave_sync();
       int hd, above;
       const int dig = find_digit(hist, need, &hd, &above);
-      __syncthreads();
+      wave_sync();
       prefix |= (u64)dig << shift;
       pmask |= 0xffull << shift;
       need -= above;
@@ -358,6 +288,82 @@ __device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* ou
     if (sel && pos < R) out[pos] = k;  // exactly R keys qualify
     base += __popcll(bs);
   }
+}
+
+// Select the R largest of n register-resident values under (value desc,
+// index asc); val[v] holds element v*64 + lane, and 0 pads the lanes past n
+// (every real value is nonzero).  The R-th largest value T is found by a
+// bitwise search below the leading bits all values share: a bit is kept
+// when at least R values are >= the candidate threshold, and the search
+// stops as soon as exactly R qualify.  Counting is one compare per register
+// plus a scalar popcount of the wave's ballot (measured faster than
+// per-lane counts with a wave reduction, and than finishing on a compacted
+// subset).  Values equal to T are taken by smallest index.  The R keys are
+// written to out[0..R) in index order.
+template <int VPL>
+__device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, u64* out) {
+  const int lane = threadIdx.x & 63;
+  const u64 lt = (1ull << lane) - 1ull;
+  auto count_ge = [&](unsigned thr) {  // thr > 0, so padding never counts
+    int c = 0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) c += __popcll(__ballot(val[v] >= thr));
+    return c;
+  };
+  unsigned T = 1;  // R >= n: every value (all are >= 1) is taken
+  int need = R;    // values equal to T still to take, by index
+  if (R < n) {
+    unsigned mx = 0, mn = 0xffffffffu;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      mx = max(mx, val[v]);
+      mn = min(mn, v * 64 + lane < n ? val[v] : 0xffffffffu);
+    }
+    mx = wave_umax(mx);
+    mn = wave_umin(mn);
+    const unsigned diff = mx ^ mn;
+    T = mx;  // all values equal: take the first R by index
+    if (diff != 0) {
+      const int hb = 31 - __clz(diff);
+      T = mx & ~((2u << hb) - 1u);  // shared prefix, lower bits zero: count(>= T) = n
+      for (int bit = hb; bit >= 0; --bit) {
+        const unsigned cand = T | (1u << bit);
+        const int c = count_ge(cand);
+        if (c >= R) {
+          T = cand;
+          if (c == R) break;
+        }
+      }
+    }
+    need = R - (T == 0xffffffffu ? 0 : count_ge(T + 1u));
+  }
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int i = v * 64 + lane;
+    const bool eq = val[v] == T;
+    const u64 be = __ballot(eq);
+    const bool sel = val[v] > T || (eq && ties + __popcll(be & lt) < need);
+    ties += __popcll(be);
+    const u64 bs = __ballot(sel);
+    const int pos = base + __popcll(bs & lt);
+    if (sel && pos < R) out[pos] = ((u64)val[v] << 32) | (u64)(~(unsigned)i);
+    base += __popcll(bs);
+  }
+}
+
+__device__ __forceinline__ u64 xor_lane64(u64 v, int j) {
+  const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
+  int a, b;
+  switch (j) {  // j is a compile-time constant after unrolling
+    case 1: a = xor_lane<1>(lo); b = xor_lane<1>(hi); break;
+    case 2: a = xor_lane<2>(lo); b = xor_lane<2>(hi); break;
+    case 4: a = xor_lane<4>(lo); b = xor_lane<4>(hi); break;
+    case 8: a = xor_lane<8>(lo); b = xor_lane<8>(hi); break;
+    case 16: a = xor_lane<16>(lo); b = xor_lane<16>(hi); break;
+    default: a = xor_lane<32>(lo); b = xor_lane<32>(hi); break;
+  }
+  return ((u64)(unsigned)b << 32) | (u64)(unsigned)a;
 }
 
 // Bitonic sort (descending) of 64*V keys held by one wave: element
@@ -384,7 +390,7 @@ __device__ void wave_sort_desc(u64 (&k)[V]) {
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const bool desc = (((v * 64 + lane) & size) == 0);
-          const u64 o = __shfl_xor(k[v], j, 64);
+          const u64 o = xor_lane64(k[v], j);
           const bool lower = (lane & j) == 0;
           const bool keep_max = lower == desc;
           k[v] = keep_max ? (k[v] > o ? k[v] : o) : (k[v] < o ? k[v] : o);
@@ -427,7 +433,7 @@ __device__ void emit_topk(const u64* fs, int K, int32_t* idx, float* score, floa
   float ev[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    ev[v] = v * 64 + lane < K ? expf(key_val(k[v]) - s0) : 0.f;
+    ev[v] = v * 64 + lane < K ? __expf(key_val(k[v]) - s0) : 0.f;
     es += ev[v];
   }
   const float inv = 1.f / wave_sum(es);
@@ -459,7 +465,7 @@ inline TopkLayout topk_layout(int Nr, int Nc, int K) {
   l.o_fs = o; o += (size_t)K * 8;
   l.o_hist = o; o += 256 * 4;
   l.o_off = o; o += (size_t)(l.Kr + 1) * 4;
-  l.bytes = o;
+  l.bytes = (o + 15) & ~(size_t)15;  // slices of several tokens stay 16-byte aligned
   return l;
 }
 
@@ -478,7 +484,7 @@ __device__ __forceinline__ void log_softmax_ord(const float* s, int n, unsigned 
   m = wave_max(m);
   float e = 0.f;
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) e += v * 64 + lane < n ? expf(f[v] - m) : 0.f;
+  for (int v = 0; v < VPL; ++v) e += v * 64 + lane < n ? __expf(f[v] - m) : 0.f;
   const float lse = m + logf(wave_sum(e));
 #pragma unroll
   for (int v = 0; v < VPL; ++v) val[v] = v * 64 + lane < n ? float_ord(f[v] - lse) : 0u;
@@ -493,32 +499,37 @@ __device__ __forceinline__ void log_softmax_ord(const float* s, int n, unsigned 
 //     min(K_c, K/(a+1)) columns: a cell at ranks (a, b) has at least
 //     (a+1)(b+1) - 1 cells before it, so (a+1)(b+1) <= K is necessary.
 //  4. Top K of the candidates under (S desc, n asc); gate = softmax of S.
+// Several tokens share a workgroup (one wave each, each with its own LDS
+// slice): one-wave workgroups leave most wave slots of a CU empty.
 template <int VPL>
-__global__ __launch_bounds__(64) void router_topk(const float* __restrict__ logits, int Nr, int Nc,
-                                                  int K, const TopkLayout lay,
-                                                  int32_t* __restrict__ idx,
-                                                  float* __restrict__ score,
-                                                  float* __restrict__ gate) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits, int L, int Nr,
+                                                   int Nc, int K, const TopkLayout lay, int wpg,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ score,
+                                                   float* __restrict__ gate) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_all[];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned char* smem = smem_all + (size_t)wv * lay.bytes;
   u64* rs = (u64*)(smem + lay.o_rs);
   u64* cs = (u64*)(smem + lay.o_cs);
   u64* cand = (u64*)(smem + lay.o_cand);
   u64* fs = (u64*)(smem + lay.o_fs);
   int* hist = (int*)(smem + lay.o_hist);
   int* off = (int*)(smem + lay.o_off);
-  const int t = blockIdx.x, lane = threadIdx.x;
+  const int t = blockIdx.x * wpg + wv, lane = threadIdx.x & 63;
+  if (t >= L) return;  // whole wave leaves; no workgroup barrier follows
   const float* sr = logits + (size_t)t * (Nr + Nc);
 
   // 1-2. rows, then columns
   {
     unsigned val[VPL];
     log_softmax_ord<VPL>(sr, Nr, val);
-    select_top_regs<VPL>(val, Nr, lay.Kr, hist, rs);
+    select_top_regs<VPL>(val, Nr, lay.Kr, rs);
     log_softmax_ord<VPL>(sr + Nr, Nc, val);
-    __syncthreads();
-    select_top_regs<VPL>(val, Nc, lay.Kc, hist, cs);
+    wave_sync();
+    select_top_regs<VPL>(val, Nc, lay.Kc, cs);
   }
-  __syncthreads();
+  wave_sync();
   wave_sort_lds(rs, lay.Kr);
   wave_sort_lds(cs, lay.Kc);
   {
@@ -527,12 +538,7 @@ __global__ __launch_bounds__(64) void router_topk(const float* __restrict__ logi
     const int a0 = lane * per;
     int loc = 0;
     for (int a = a0; a < a0 + per && a < lay.Kr; ++a) loc += min(lay.Kc, K / (a + 1));
-    int inc = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += v;
-    }
+    const int inc = wave_incl_scan(loc);
     int run = inc - loc;
     for (int a = a0; a < a0 + per && a < lay.Kr; ++a) {
       off[a] = run;
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(64) void router_topk(const float* __restrict__ logi
     }
     if (lane == 63) off[lay.Kr] = inc;
   }
-  __syncthreads();
+  wave_sync();
 
   // 3. candidate c belongs to the row rank a with off[a] <= c < off[a+1]
   for (int c = lane; c < lay.P; c += 64) {
@@ -553,11 +559,11 @@ __global__ __launch_bounds__(64) void router_topk(const float* __restrict__ logi
     const u64 rk = rs[lo], ck = cs[c - off[lo]];
     cand[c] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
   }
-  __syncthreads();
+  wave_sync();
 
   // 4. top K of the candidates, ordered, gated and written
   select_top_lds(cand, lay.P, K, hist, fs);
-  __syncthreads();
+  wave_sync();
   int32_t* io = idx + (size_t)t * K;
   float* so = score + (size_t)t * K;
   float* go = gate + (size_t)t * K;
@@ -590,12 +596,14 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
                               float* score, float* gate, hipStream_t s) {
   const TopkLayout lay = topk_layout(Nr, Nc, K);
   const int need = (max(Nr, Nc) + 63) / 64;  // values per lane
-  // at most K*(2 + H(K)) + K keys: under 40 KB for K <= 512
+  // per token at most K*(3 + H(K)) keys: under 42 KB for K <= 512; up to
+  // four tokens share a workgroup within the default 64 KB of dynamic LDS
   const size_t lds = lay.bytes;
+  const int wpg = lds * 4 <= 65536 ? 4 : lds * 2 <= 65536 ? 2 : 1;
 #define OMNI_TOPK(V)                                                                           \
   if (need <= V) {                                                                             \
-    hipLaunchKernelGGL(router_topk<V>, dim3(L), dim3(64), lds, s, logits, Nr, Nc, K, lay, idx, \
-                       score, gate);                                                           \
+    hipLaunchKernelGGL(router_topk<V>, dim3((L + wpg - 1) / wpg), dim3(64 * wpg), lds * wpg, s, \
+                       logits, L, Nr, Nc, K, lay, wpg, idx, score, gate);                     \
     return hipGetLastError();                                                                  \
   }
   OMNI_TOPK(1) OMNI_TOPK(2) OMNI_TOPK(4) OMNI_TOPK(8) OMNI_TOPK(12) OMNI_TOPK(16) OMNI_TOPK(24)

@@ -62,12 +62,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(int* __restri
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = i0 + q < ntiles ? row[i0 + q] : 0;
     const int s = v[0] + v[1] + v[2] + v[3];
-    int inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += u;
-    }
+    const int inc = wave_incl_scan(s);
     if (lane == 63) wsum[wave] = inc;
     __syncthreads();
     int woff = 0, tot = 0;
@@ -106,12 +101,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
       v[q] = 4 * lane + q < radix ? totals[4 * lane + q] : 0;
       s += v[q];
     }
-    int inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += u;
-    }
+    const int inc = wave_incl_scan(s);
     int b = inc - s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
