@@ -119,6 +119,153 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t* __restri
     }
 }
 
+// ------------------------------------------------------------------ bf16 GEMM, pipelined
+// The same 128 x 128 tile and wave layout, with the k-tiles (BK deep)
+// streamed through S LDS stages by direct global->LDS loads
+// (global_load_lds_dwordx4: each instruction writes 64 lanes x 16 bytes of
+// LDS without register staging), so S-1 k-tiles are in flight while one is
+// multiplied.  A stage holds the A and B tiles as 128 rows x 2*BK bytes; the
+// 16-byte chunk c of row r sits in slot c ^ swz(r), which spreads the 16
+// rows read by one ds_read_b128 over 16 distinct bank groups.  Rows past L
+// or N_r+N_c are loaded from a clamped row (their results are never
+// stored).  Needs d % BK == 0 (no partial k-tile).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most n loads of this wave are outstanding (n a multiple of
+// the loads per k-tile: 4 or 8).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+  }
+}
+
+// Workgroup barrier without the fence of __syncthreads (which would also
+// wait for every direct-to-LDS load still in flight).
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier after this wave's LDS reads of a stage have completed, so that no
+// wave refills the stage while another still reads it.
+__device__ __forceinline__ void block_sync_reads_done() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BK>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (BK == 64) return (r >> 1) & 7;  // 8 chunks per 128-byte row
+  else return (r >> 2) & 3;                     // 4 chunks per 64-byte row
+}
+
+template <int BK, int S>
+__global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ Wr,
+                                                             const uint16_t* __restrict__ Wc,
+                                                             int L, int d, int Nr, int Nc,
+                                                             float* __restrict__ C) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
+  constexpr int ROWB = 2 * BK;           // bytes per tile row
+  constexpr int TILEB = 128 * ROWB;      // bytes of the A (or B) tile
+  constexpr int STAGE = 2 * TILEB;
+  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;          // rows per 1 KB load instruction
+  constexpr int LPW = TILEB / 1024 / 4;  // loads per wave per tile (A or B)
+  const int Ntot = Nr + Nc;
+  const int tile_m = blockIdx.y * 128, tile_n = blockIdx.x * 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  // load j of wave w fills bytes [(LPW*w + j) * 1024, +1024) of a tile
+  const uint16_t* asrc[LPW];
+  const uint16_t* bsrc[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = (wave * LPW + j) * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
+    const int gm = min(tile_m + r, L - 1);
+    const int gn = min(tile_n + r, Ntot - 1);
+    asrc[j] = x + (size_t)gm * d + chunk * 8;
+    bsrc[j] = (gn < Nr ? Wr + (size_t)gn * d : Wc + (size_t)(gn - Nr) * d) + chunk * 8;
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = gsm + (kt % S) * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[j] + k0),
+                                       (lds_void*)(st + (wave * LPW + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + k0),
+                                       (lds_void*)(st + TILEB + (wave * LPW + j) * 1024), 16, 0,
+                                       0);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = d / BK;
+  for (int kt = 0; kt < S - 1 && kt < nk; ++kt) issue(kt);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+    wait_vm(2 * LPW * min(S - 1, nk - 1 - kt));  // this wave's loads of tile kt are done
+    block_sync_lds();                            // ... and every wave's
+    const unsigned char* st = gsm + (kt % S) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int kc = ks * 4 + (lane >> 4);  // 16-byte chunk of the k-slice
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + i * 16 + (lane & 15);
+        af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn + j * 16 + (lane & 15);
+        bfr[j] = *(const bf16x8*)(st + TILEB + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    block_sync_reads_done();  // stage kt % S is refilled at the next iteration
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = tile_n + wn + j * 16 + (lane & 15);
+      if (col >= Ntot) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = tile_m + wm + i * 16 + (lane >> 4) * 4 + r;
+        if (row < L) C[(size_t)row * Ntot + col] = acc[i][j][r];
+      }
+    }
+}
+
+// Measured on 4096 x 2048 x 2608: BK = 64 with 2 stages (64 KB of LDS, two
+// workgroups per CU) beats deeper pipelines, whose larger LDS footprint
+// leaves one workgroup per CU (70 us against 78-90 us; 85 us unpipelined).
+constexpr int GEMM_BK = 64, GEMM_STAGES = 2;
+
 // ------------------------------------------------------------------ fp32 GEMM
 // fp32 inputs: plain LDS-tiled VALU GEMM, 64 x 64 tile, 4 x 4 outputs/thread.
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -578,7 +725,13 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
 hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int L, int d,
                               int Nr, int Nc, omni_dtype dt, float* logits, hipStream_t s) {
   const int Ntot = Nr + Nc;
-  if (dt == OMNI_BF16) {
+  if (dt == OMNI_BF16 && d % GEMM_BK == 0) {
+    constexpr int S = GEMM_STAGES, BK = GEMM_BK;
+    dim3 grid((Ntot + 127) / 128, (L + 127) / 128);
+    hipLaunchKernelGGL((router_gemm_bf16_pipe<BK, S>), grid, dim3(256), S * 2 * 128 * 2 * BK, s,
+                       (const uint16_t*)x, (const uint16_t*)Wr, (const uint16_t*)Wc, L, d, Nr, Nc,
+                       logits);
+  } else if (dt == OMNI_BF16) {  // d not a multiple of BK: zero-filled partial k-tile
     dim3 grid((Ntot + GBN - 1) / GBN, (L + GBM - 1) / GBM);
     hipLaunchKernelGGL(router_gemm_bf16, grid, dim3(256), 0, s, (const uint16_t*)x,
                        (const uint16_t*)Wr, (const uint16_t*)Wc, L, d, Nr, Nc, logits);
