@@ -155,6 +155,23 @@ omni_status omni_expert_forward(const void* x, const void* W, const void* V, con
   return hip_status(e, "expert output launch");
 }
 
+omni_status omni_expert_forward_token_centric(const void* x, const void* W, const void* V,
+                                              const int32_t* idx, const float* gate, int64_t L,
+                                              int64_t d, int64_t N, int64_t K, omni_dtype dt,
+                                              float* y, void* stream) {
+  size_t need = 0;
+  omni_status s = expert_ws(L, d, N, K, dt, &need);  // same size rules; no workspace used
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !y)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward_token_centric: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(y))
+    return fail(OMNI_ERR_INVALID_ARG,
+                "omni_expert_forward_token_centric: x, W, V and y must be 16-byte aligned");
+  hipError_t e = omni::launch_expert_tc(x, W, V, idx, gate, (int)L, (int)d, (int)K, dt, y,
+                                        (hipStream_t)stream);
+  return hip_status(e, "token-centric expert launch");
+}
+
 omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
                                  int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
   if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");

@@ -212,6 +212,112 @@ __global__ __launch_bounds__(512) void expert_out(const uint16_t* __restrict__ V
   for (int i = 0; i < E; i += 4) *(f32x4*)(yo + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
 }
 
+// ------------------------------------------------------------------ token-centric baseline
+// The execution order the pages compare against (makerbund section 5: the
+// ablation that reverts expert-centric scheduling): each token fetches the
+// rows of its own K experts, with no schedule.  One workgroup per token:
+// wave w computes a_k = g_k * SiLU(x_t . W[e_k]) for k = w, w+4, ... (x_t held
+// in registers, TC_ROWS W rows in flight), the K activations meet in LDS, and
+// the V pass is the one of expert_out.
+constexpr int TC_ROWS = 4;
+
+template <bool BF16, int NCH>
+__global__ __launch_bounds__(256) void expert_tc(const uint16_t* __restrict__ x_,
+                                                 const uint16_t* __restrict__ W_,
+                                                 const uint16_t* __restrict__ V_,
+                                                 const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ gate, int d, int K,
+                                                 float* __restrict__ y) {
+  using V = Vec<BF16>;
+  constexpr int E = V::E;
+  __shared__ int se[OMNI_MAX_K];
+  __shared__ float sa[OMNI_MAX_K];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int k = tid; k < K; k += 256) se[k] = idx[(size_t)t * K + k];
+  __syncthreads();
+
+  const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
+  const unsigned cb = lane * 16u;
+  u32x4 xr[NCH];
+  {
+    const char* base = (const char*)x_ + (size_t)t * row_bytes;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const unsigned o = c * 1024u + cb;
+      xr[c] = o < row_bytes ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // W pass: rows k = wave + 4*(r0 + q), TC_ROWS at a time
+  for (int k0 = wave; k0 < K; k0 += 4 * TC_ROWS) {
+    u32x4 w[TC_ROWS][NCH];
+#pragma unroll
+    for (int q = 0; q < TC_ROWS; ++q) {
+      const int k = k0 + 4 * q;
+      const char* base = (const char*)W_ + (size_t)uni(se[k < K ? k : k0]) * row_bytes;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const unsigned o = c * 1024u + cb;
+        w[q][c] = (k < K && o < row_bytes) ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TC_ROWS; ++q) {
+      const int k = k0 + 4 * q;
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) part += V::dot(xr[c], w[q][c]);
+      const float h = wave_sum(part);
+      if (lane == 0 && k < K) sa[k] = gate[(size_t)t * K + k] * (h / (1.f + expf(-h)));
+    }
+  }
+  __syncthreads();
+  // V pass: each thread owns 16 bytes of y's row
+  for (int c0 = tid * E; c0 < d; c0 += 256 * E) {
+    const unsigned ob = (unsigned)c0 * (BF16 ? 2u : 4u);
+    float acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = 0.f;
+    int k = 0;
+    for (; k + OUT_UNROLL <= K; k += OUT_UNROLL) {
+      u32x4 v[OUT_UNROLL];
+#pragma unroll
+      for (int j = 0; j < OUT_UNROLL; ++j)
+        v[j] = ld16_nt((const char*)V_ + (size_t)uni(se[k + j]) * row_bytes + ob);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < OUT_UNROLL; ++j) V::axpy(uni(sa[k + j]), v[j], acc);
+    }
+    for (; k < K; ++k)
+      V::axpy(uni(sa[k]), ld16_nt((const char*)V_ + (size_t)uni(se[k]) * row_bytes + ob), acc);
+    float* yo = y + (size_t)t * d + c0;
+#pragma unroll
+    for (int i = 0; i < E; i += 4) *(f32x4*)(yo + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+  }
+}
+
+template <bool BF16>
+hipError_t launch_tc_t(const void* x, const void* W, const void* V, const int32_t* idx,
+                       const float* gate, int L, int d, int K, float* y, hipStream_t s) {
+  const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
+  const int nch = (int)((row_bytes + 1023) / 1024);
+  const uint16_t* xp = (const uint16_t*)x;
+  const uint16_t* wp = (const uint16_t*)W;
+  const uint16_t* vp = (const uint16_t*)V;
+#define OMNI_TC(N)                                                                           \
+  case N:                                                                                    \
+    hipLaunchKernelGGL((expert_tc<BF16, N>), dim3(L), dim3(256), 0, s, xp, wp, vp, idx, gate, \
+                       d, K, y);                                                             \
+    break;
+  switch (nch) {
+    OMNI_TC(1) OMNI_TC(2) OMNI_TC(3) OMNI_TC(4) OMNI_TC(5) OMNI_TC(6) OMNI_TC(7) OMNI_TC(8)
+    default:
+      return hipErrorInvalidValue;  // d above the validated limit
+  }
+#undef OMNI_TC
+  return hipGetLastError();
+}
+
 template <bool BF16>
 hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const float* gate,
                         const int32_t* perm, int M, int d, int K, float* act, hipStream_t s) {
@@ -243,6 +349,13 @@ hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, c
   const int M = L * K;
   return dt == OMNI_BF16 ? launch_act_t<true>(x, W, idx, gate, perm, M, d, K, act, s)
                          : launch_act_t<false>(x, W, idx, gate, perm, M, d, K, act, s);
+}
+
+hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,
+                            const float* gate, int L, int d, int K, omni_dtype dt, float* y,
+                            hipStream_t s) {
+  return dt == OMNI_BF16 ? launch_tc_t<true>(x, W, V, idx, gate, L, d, K, y, s)
+                         : launch_tc_t<false>(x, W, V, idx, gate, L, d, K, y, s);
 }
 
 hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,

@@ -138,6 +138,10 @@ hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedP
 hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, const float* gate,
                              const int32_t* perm, int L, int d, int K, omni_dtype dt,
                              float* act, hipStream_t s);
+// token-centric baseline: y[t] = sum_k gate * SiLU(x_t . W[e]) * V[e], one token per workgroup
+hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,
+                            const float* gate, int L, int d, int K, omni_dtype dt, float* y,
+                            hipStream_t s);
 // y[t] = sum_k act[t*K+k] * V[idx[t*K+k]]
 hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,
                              int K, omni_dtype dt, float* y, hipStream_t s);

@@ -21,8 +21,9 @@ _ABI_VERSION = 1
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
-EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward", "omni_workspace_bytes",
-            "omni_status_string", "omni_last_error", "omni_abi_version")
+EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward",
+            "omni_expert_forward_token_centric", "omni_workspace_bytes", "omni_status_string",
+            "omni_last_error", "omni_abi_version")
 
 
 class OmniError(RuntimeError):
@@ -50,9 +51,12 @@ def library() -> ctypes.CDLL:
     lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         ctypes.c_int, vp, vp, sz, vp]
+    lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                      ctypes.c_int, vp, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
-    for f in ("omni_router", "omni_schedule", "omni_expert_forward", "omni_workspace_bytes"):
+    for f in ("omni_router", "omni_schedule", "omni_expert_forward",
+              "omni_expert_forward_token_centric", "omni_workspace_bytes"):
         getattr(lib, f).restype = ctypes.c_int
     lib.omni_status_string.argtypes = [ctypes.c_int]
     lib.omni_status_string.restype = ctypes.c_char_p
@@ -175,6 +179,25 @@ def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None):
     pw, nw = _workspace(ws, need, x.device)
     _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, L, d, N, K, dt, py, pw, nw,
                                          _stream(stream)), "omni_expert_forward")
+    return y
+
+
+def omni_expert_forward_token_centric(x, W, V, idx, gate, y=None, stream=None):
+    """Token-centric baseline of the assembly (no schedule) -> y [L, d] float32."""
+    L, d = x.shape
+    N = W.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    px = _dev(x, "x")
+    pW = _dev(W, "W", x.dtype, (N, d))
+    pV = _dev(V, "V", x.dtype, (N, d))
+    pi = _dev(idx, "idx", torch.int32, (L, K))
+    pg = _dev(gate, "gate", torch.float32, (L, K))
+    y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
+    py = _dev(y, "y", torch.float32, (L, d))
+    _check(library().omni_expert_forward_token_centric(px, pW, pV, pi, pg, L, d, N, K, dt, py,
+                                                       _stream(stream)),
+           "omni_expert_forward_token_centric")
     return y
 
 

@@ -238,6 +238,22 @@ def main():
         },
         "router_gemm_flops": router_flops,
     }
+    # the token-centric order the expert-centric schedule replaces, timed on
+    # the same routing (same y up to rounding)
+    tc_times = []
+    y_tc = torch.empty_like(br.y)
+    for i in range(args.steps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate, y_tc)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            tc_times.append(e0.elapsed_time(e1))
+    tc_ms = statistics.median(tc_times)
+    out["token_centric_assembly_ms"] = round(tc_ms, 4)
+    out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
+
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_sample_tokens, args.seed)

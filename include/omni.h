@@ -7,6 +7,7 @@
  *   omni_router          Cartesian Product Router: ids, scores, gates
  *   omni_schedule        expert-centric schedule: sorted tasks, group offsets
  *   omni_expert_forward  Dynamic Expert Assembly: y
+ * and one comparison baseline, omni_expert_forward_token_centric.
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller, row-major and
@@ -144,6 +145,22 @@ OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const voi
                                 int64_t L, int64_t d, int64_t N, int64_t K,
                                 omni_dtype dt, float* y,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_expert_forward_token_centric - the same y as omni_expert_forward,
+ * computed in token-centric order: each token fetches the W and V rows of
+ * its own K experts, with no schedule.  This is the execution order that the
+ * expert-centric scheduling replaces (makerbund article, section 5: the
+ * ablation that reverts to token-centric execution keeps the quality and
+ * costs latency); it is provided as the measured baseline for that
+ * comparison.  Arguments as for omni_expert_forward, without perm and
+ * without workspace.  y is fully overwritten.
+ */
+OMNI_API omni_status omni_expert_forward_token_centric(const void* x, const void* W,
+                                                       const void* V, const int32_t* idx,
+                                                       const float* gate, int64_t L, int64_t d,
+                                                       int64_t N, int64_t K, omni_dtype dt,
+                                                       float* y, void* stream);
 
 /*
  * omni_workspace_bytes - workspace size needed by one call of `op` with

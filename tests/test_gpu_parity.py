@@ -123,6 +123,27 @@ def test_expert_forward_on_oracle_routing():
     check_y(y, y_o, RTOL["f32"])
 
 
+@pytest.mark.parametrize("case", [(64, 64, 32, 32, 16, 16, "f32"), (130, 72, 37, 29, 50, 7, "bf16"),
+                                  (200, 520, 300, 301, 128, 128, "bf16"),
+                                  (16, 4096, 64, 64, 32, 64, "bf16"), (24, 2048, 40, 40, 20, 16, "f32"),
+                                  (40, 64, 600, 700, 512, 512, "bf16")],
+                         ids=lambda c: "L{}_d{}_{}x{}_K{}_B{}_{}".format(*c))
+def test_token_centric_baseline_matches_oracle(case):
+    L, d, Nr, Nc, K, B, dt = case
+    w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, B, dt, seed=zlib.crc32(repr(case).encode()) % 1000)
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    say(f"token-centric {w.name}")
+    br = run_branch(inp, w)
+    y_tc = omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate)
+    torch.cuda.synchronize()
+    y_o = O.assemble_token_centric(inp_cpu["x"], inp_cpu["W"], inp_cpu["V"], to_np(br.idx),
+                                   to_np(br.gate))
+    check_y(y_tc, y_o, RTOL_FP32_ARITH)
+    # same k-order sum of the V pass: equal to the expert-centric path up to
+    # the rounding of the activations' dot products
+    check_y(y_tc, to_np(br.y), RTOL_FP32_ARITH)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = synth.WORKLOADS[synth.TINY]
     inp = {k: v.cuda() for k, v in synth.make_inputs(w, seed=5).items()}
@@ -174,5 +195,10 @@ def test_full_size_workload_sampled(name):
                                    idx, to_np(br.gate)[toks])
     nrm, mx = check_y(to_np(br.y)[toks], y_o, min(RTOL[w.dtype], RTOL_FP32_ARITH))
     say(f"  swaps={swaps} over {len(toks)} tokens; y_err norm={nrm:.2e} max={mx:.2e}")
+    # token-centric baseline on the same routing, whole y against the method's
+    y_tc = omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate)
+    torch.cuda.synchronize()
+    dy = (y_tc - br.y).norm() / br.y.norm()
+    assert dy.item() <= RTOL_FP32_ARITH, dy.item()
     del inp, br
     torch.cuda.empty_cache()
