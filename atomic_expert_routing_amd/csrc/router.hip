@@ -153,14 +153,6 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("" ::: "memory");
 }
 
-// Barrier after this wave's LDS reads of a stage have completed, so that no
-// wave refills the stage while another still reads it.
-__device__ __forceinline__ void block_sync_reads_done() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int BK>
 __device__ __forceinline__ int chunk_swz(int r) {
   if constexpr (BK == 64) return (r >> 1) & 7;  // 8 chunks per 128-byte row
@@ -218,34 +210,42 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // fragments of k-step ks of a stage: A rows wm.., B rows wn.. of the tile
+  auto load_frags = [&](const unsigned char* st, int ks, bf16x8* af, bf16x8* bfr) {
+    const int kc = ks * 4 + (lane >> 4);  // 16-byte chunk of the k-slice
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + i * 16 + (lane & 15);
+      af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn + j * 16 + (lane & 15);
+      bfr[j] = *(const bf16x8*)(st + TILEB + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
+    }
+  };
+
   const int nk = d / BK;
   for (int kt = 0; kt < S - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
+    // tile kt landed for this wave; after the barrier it has for every wave,
+    // and every wave has finished reading tile kt-1, whose stage is refilled
+    wait_vm(2 * LPW * min(S - 2, nk - 1 - kt));
+    block_sync_lds();
     if (kt + S - 1 < nk) issue(kt + S - 1);
-    wait_vm(2 * LPW * min(S - 1, nk - 1 - kt));  // this wave's loads of tile kt are done
-    block_sync_lds();                            // ... and every wave's
     const unsigned char* st = gsm + (kt % S) * STAGE;
+    bf16x8 af[2][4], bfr[2][4];
+    load_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      const int kc = ks * 4 + (lane >> 4);  // 16-byte chunk of the k-slice
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm + i * 16 + (lane & 15);
-        af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn + j * 16 + (lane & 15);
-        bfr[j] = *(const bf16x8*)(st + TILEB + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
-      }
+      if (ks + 1 < BK / 32) load_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                              acc[i][j], 0, 0, 0);
     }
-    block_sync_reads_done();  // stage kt % S is refilled at the next iteration
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -263,7 +263,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
 
 // Measured on 4096 x 2048 x 2608: BK = 64 with 2 stages (64 KB of LDS, two
 // workgroups per CU) beats deeper pipelines, whose larger LDS footprint
-// leaves one workgroup per CU (70 us against 78-90 us; 85 us unpipelined).
+// leaves one workgroup per CU (64 us against 76-88 us; 85 us with register
+// staging).
 constexpr int GEMM_BK = 64, GEMM_STAGES = 2;
 
 // ------------------------------------------------------------------ fp32 GEMM
