@@ -133,16 +133,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Wait until at most n loads of this wave are outstanding (n a multiple of
 // the loads per k-tile: 4 or 8).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+template <int N>
+__device__ __forceinline__ void wait_vm_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most i * N of this wave's vector loads are outstanding
+// (i = 0 .. MAXI, the k-tiles allowed to stay in flight; N loads per k-tile).
+template <int N, int MAXI>
+__device__ __forceinline__ void wait_vm_tiles(int i) {
+  if constexpr (MAXI >= 3) {
+    if (i >= 3) return wait_vm_imm<3 * N>();
   }
+  if constexpr (MAXI >= 2) {
+    if (i >= 2) return wait_vm_imm<2 * N>();
+  }
+  if constexpr (MAXI >= 1) {
+    if (i >= 1) return wait_vm_imm<N>();
+  }
+  wait_vm_imm<0>();
 }
 
 // Workgroup barrier without the fence of __syncthreads (which would also
@@ -159,56 +169,75 @@ __device__ __forceinline__ int chunk_swz(int r) {
   else return (r >> 2) & 3;                     // 4 chunks per 64-byte row
 }
 
-template <int BK, int S>
+// Tiles are 128 x (32 NJ): 4 waves as 2 x 2, each 64 x 16 NJ outputs held as
+// 4 x NJ MFMA 16x16 accumulators.  The grid is one-dimensional and the tile
+// order is XCD-aware: workgroup b runs on XCD b % 8 and takes tile
+// (b % 8) * per_xcd + b / 8 of the row-major tile order, so that each XCD
+// sweeps a contiguous band of output rows and the x and W panels its
+// concurrent workgroups share are fetched into its own L2 once.
+template <int BK, int S, int NJ>
 __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __restrict__ x,
                                                              const uint16_t* __restrict__ Wr,
                                                              const uint16_t* __restrict__ Wc,
                                                              int L, int d, int Nr, int Nc,
+                                                             int tiles_n, int per_xcd,
                                                              float* __restrict__ C) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
-  constexpr int ROWB = 2 * BK;           // bytes per tile row
-  constexpr int TILEB = 128 * ROWB;      // bytes of the A (or B) tile
-  constexpr int STAGE = 2 * TILEB;
-  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;          // rows per 1 KB load instruction
-  constexpr int LPW = TILEB / 1024 / 4;  // loads per wave per tile (A or B)
+  constexpr int TN = 32 * NJ;             // tile columns
+  constexpr int ROWB = 2 * BK;            // bytes per tile row
+  constexpr int TILEA = 128 * ROWB;       // bytes of the A tile
+  constexpr int TILEB = TN * ROWB;        // bytes of the B tile
+  constexpr int STAGE = TILEA + TILEB;
+  constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;           // rows per 1 KB load instruction
+  constexpr int LPWA = TILEA / 1024 / 4;  // loads per wave per k-tile, A
+  constexpr int LPWB = TILEB / 1024 / 4;  // and B
+  static_assert(TILEB % 4096 == 0, "B tile must split into 1 KB loads over 4 waves");
+  static_assert(S >= 2 && S <= 5, "pipeline depth");
   const int Ntot = Nr + Nc;
-  const int tile_m = blockIdx.y * 128, tile_n = blockIdx.x * 128;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int tiles_m = (L + 127) / 128;
+  if (t >= tiles_m * tiles_n) return;  // whole workgroup, before any barrier
+  const int tile_m = (t / tiles_n) * 128, tile_n = (t % tiles_n) * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (16 * NJ);
 
   // load j of wave w fills bytes [(LPW*w + j) * 1024, +1024) of a tile
-  const uint16_t* asrc[LPW];
-  const uint16_t* bsrc[LPW];
+  const uint16_t* asrc[LPWA];
+  const uint16_t* bsrc[LPWB];
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = (wave * LPW + j) * RPI + lane / CPR;
+  for (int j = 0; j < LPWA; ++j) {
+    const int r = (wave * LPWA + j) * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    const int gm = min(tile_m + r, L - 1);
+    asrc[j] = x + (size_t)min(tile_m + r, L - 1) * d + chunk * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < LPWB; ++j) {
+    const int r = (wave * LPWB + j) * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
     const int gn = min(tile_n + r, Ntot - 1);
-    asrc[j] = x + (size_t)gm * d + chunk * 8;
     bsrc[j] = (gn < Nr ? Wr + (size_t)gn * d : Wc + (size_t)(gn - Nr) * d) + chunk * 8;
   }
   auto issue = [&](int kt) {
     unsigned char* st = gsm + (kt % S) * STAGE;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
+    for (int j = 0; j < LPWA; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(asrc[j] + k0),
-                                       (lds_void*)(st + (wave * LPW + j) * 1024), 16, 0, 0);
+                                       (lds_void*)(st + (wave * LPWA + j) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
+    for (int j = 0; j < LPWB; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + k0),
-                                       (lds_void*)(st + TILEB + (wave * LPW + j) * 1024), 16, 0,
-                                       0);
+                                       (lds_void*)(st + TILEA + (wave * LPWB + j) * 1024), 16,
+                                       0, 0);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // fragments of k-step ks of a stage: A rows wm.., B rows wn.. of the tile
   auto load_frags = [&](const unsigned char* st, int ks, bf16x8* af, bf16x8* bfr) {
@@ -219,9 +248,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
       af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int r = wn + j * 16 + (lane & 15);
-      bfr[j] = *(const bf16x8*)(st + TILEB + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
+      bfr[j] = *(const bf16x8*)(st + TILEA + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
     }
   };
 
@@ -230,11 +259,11 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt landed for this wave; after the barrier it has for every wave,
     // and every wave has finished reading tile kt-1, whose stage is refilled
-    wait_vm(2 * LPW * min(S - 2, nk - 1 - kt));
+    wait_vm_tiles<LPWA + LPWB, S - 2>(min(S - 2, nk - 1 - kt));
     block_sync_lds();
     if (kt + S - 1 < nk) issue(kt + S - 1);
     const unsigned char* st = gsm + (kt % S) * STAGE;
-    bf16x8 af[2][4], bfr[2][4];
+    bf16x8 af[2][4], bfr[2][NJ];
     load_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
@@ -242,7 +271,7 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][j],
                                                               acc[i][j], 0, 0, 0);
     }
@@ -250,7 +279,7 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int col = tile_n + wn + j * 16 + (lane & 15);
       if (col >= Ntot) continue;
 #pragma unroll
@@ -261,11 +290,12 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
     }
 }
 
-// Measured on 4096 x 2048 x 2608: BK = 64 with 2 stages (64 KB of LDS, two
-// workgroups per CU) beats deeper pipelines, whose larger LDS footprint
-// leaves one workgroup per CU (64 us against 76-88 us; 85 us with register
-// staging).
-constexpr int GEMM_BK = 64, GEMM_STAGES = 2;
+// Measured on 4096 x 2048 x 2608 (all with the XCD-aware order, which alone
+// takes the 128 x 128 tile from 64 to 60 us): 128 x 192 tiles, BK = 64 and
+// 2 stages (80 KB of LDS, two workgroups per CU; 448 tiles fill the 512
+// workgroup slots in one round) 54 us; 128 x 160 67 us; 128 x 192 with BK = 32
+// and 2 or 3 stages 57-61 us; 128 x 128 with BK = 32 and 4 stages 71 us.
+constexpr int GEMM_BK = 64, GEMM_STAGES = 2, GEMM_NJ = 6;
 
 // ------------------------------------------------------------------ fp32 GEMM
 // fp32 inputs: plain LDS-tiled VALU GEMM, 64 x 64 tile, 4 x 4 outputs/thread.
@@ -727,11 +757,14 @@ hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int
                               int Nr, int Nc, omni_dtype dt, float* logits, hipStream_t s) {
   const int Ntot = Nr + Nc;
   if (dt == OMNI_BF16 && d % GEMM_BK == 0) {
-    constexpr int S = GEMM_STAGES, BK = GEMM_BK;
-    dim3 grid((Ntot + 127) / 128, (L + 127) / 128);
-    hipLaunchKernelGGL((router_gemm_bf16_pipe<BK, S>), grid, dim3(256), S * 2 * 128 * 2 * BK, s,
+    constexpr int S = GEMM_STAGES, BK = GEMM_BK, NJ = GEMM_NJ;
+    const int tiles_n = (Ntot + 32 * NJ - 1) / (32 * NJ);
+    const int tiles = ((L + 127) / 128) * tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const size_t lds = (size_t)S * (128 + 32 * NJ) * 2 * BK;
+    hipLaunchKernelGGL((router_gemm_bf16_pipe<BK, S, NJ>), dim3(8 * per_xcd), dim3(256), lds, s,
                        (const uint16_t*)x, (const uint16_t*)Wr, (const uint16_t*)Wc, L, d, Nr, Nc,
-                       logits);
+                       tiles_n, per_xcd, logits);
   } else if (dt == OMNI_BF16) {  // d not a multiple of BK: zero-filled partial k-tile
     dim3 grid((Ntot + GBN - 1) / GBN, (L + GBM - 1) / GBM);
     hipLaunchKernelGGL(router_gemm_bf16, grid, dim3(256), 0, s, (const uint16_t*)x,
