@@ -16,6 +16,10 @@ The roofline entry covers the expert-assembly call (its two kernels:
 expert_act and expert_out), whose algorithmic bytes are the unique W and V
 rows gathered, x read once, y written once and 12 bytes of task metadata
 per task; the unique expert count is taken from the step's own ids.
+After the timed steps, --cold-steps more steps each follow a 512 MiB device
+fill that evicts the 256 MB Infinity Cache; their per-stage medians are
+reported as cold_cache_ms_median (the timed value is the warm, back-to-back
+rate).
 
 cpu_baseline: the float64 CPU oracle timed on this host on a bounded sample
 of the same workload's tokens, scaled to the full token count.
@@ -48,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
                     help="tokens the CPU oracle routes and assembles (capped at L)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps, each after a 512 MiB write that evicts the 256 MB "
+                         "Infinity Cache, timed with events (0 to skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB "
                          "(reference kernel for scaling hardware byte counters)")
@@ -192,6 +199,7 @@ def main():
         return statistics.median(e[a].elapsed_time(e[b]) for e in evs)
 
     router_ms, sched_ms, expert_ms = med(0, 1), med(1, 2), med(2, 3)
+    step_min_ms = min(e[0].elapsed_time(e[3]) for e in evs)
     expert_mean_ms = statistics.fmean(e[2].elapsed_time(e[3]) for e in evs)
     step_ev_ms = med(0, 3)
 
@@ -238,6 +246,24 @@ def main():
         },
         "router_gemm_flops": router_flops,
     }
+    # cold cache: before each of these steps a 512 MiB fill evicts the 256 MB
+    # Infinity Cache (and every L2); the events bracket the step alone
+    if args.cold_steps:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append([ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
+                         ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[3])])
+        del flush
+        cm = [statistics.median(c[i] for c in cold) for i in range(4)]
+        out["cold_cache_ms_median"] = {"router": round(cm[0], 4), "schedule": round(cm[1], 4),
+                                       "expert_forward": round(cm[2], 4), "step": round(cm[3], 4)}
+    out["step_events_ms_min"] = round(step_min_ms, 4)
+
     # the token-centric order the expert-centric schedule replaces, timed on
     # the same routing (same y up to rounding)
     tc_times = []
