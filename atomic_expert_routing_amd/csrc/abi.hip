@@ -88,6 +88,21 @@ omni_status expert_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt,
   return OMNI_OK;
 }
 
+omni_status expert_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
+  *out = omni::plan_expert_backward(L, d, N, K).ws_bytes;
+  return OMNI_OK;
+}
+
+omni_status router_bwd_ws(int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t K, omni_dtype dt,
+                          size_t* out) {
+  omni_status s;
+  if ((s = router_ws(L, d, Nr, Nc, K, dt, out)) != OMNI_OK) return s;
+  *out = omni::plan_router_backward(L, d, Nr, Nc, dt).ws_bytes;
+  return OMNI_OK;
+}
+
 omni_status check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
     return fail(OMNI_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
@@ -172,6 +187,49 @@ omni_status omni_expert_forward_token_centric(const void* x, const void* W, cons
   return hip_status(e, "token-centric expert launch");
 }
 
+omni_status omni_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
+                                 const float* gate, const float* dy, int64_t L, int64_t d,
+                                 int64_t N, int64_t K, omni_dtype dt, float* dx, float* dgate,
+                                 int32_t* uniq, int32_t* n_uniq, float* dW_rows, float* dV_rows,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = expert_bwd_ws(L, d, N, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !dy || !dx || !dgate || !uniq || !n_uniq || !dW_rows ||
+      !dV_rows)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_backward: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(dy) || !aligned16(dx) ||
+      !aligned16(dW_rows) || !aligned16(dV_rows))
+    return fail(OMNI_ERR_INVALID_ARG,
+                "omni_expert_backward: x, W, V, dy, dx, dW_rows and dV_rows must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::BwdPlan plan = omni::plan_expert_backward(L, d, N, K);
+  hipError_t e = omni::launch_expert_backward(x, W, V, idx, gate, dy, (int)L, (int)d, (int)N,
+                                              (int)K, dt, dx, dgate, uniq, n_uniq, dW_rows,
+                                              dV_rows, plan, ws, (hipStream_t)stream);
+  return hip_status(e, "expert backward launch");
+}
+
+omni_status omni_router_backward(const void* x, const void* Wr, const void* Wc,
+                                 const int32_t* idx, const float* gate, const float* dgate,
+                                 int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t K,
+                                 omni_dtype dt, float* dx, float* dWr, float* dWc, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !Wr || !Wc || !idx || !gate || !dgate || !dx || !dWr || !dWc)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_router_backward: NULL array pointer");
+  if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wc) || !aligned16(dx))
+    return fail(OMNI_ERR_INVALID_ARG, "omni_router_backward: x, Wr, Wc and dx must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::RouterBwdPlan plan = omni::plan_router_backward(L, d, Nr, Nc, dt);
+  hipError_t e = omni::launch_router_backward(x, Wr, Wc, idx, gate, dgate, (int)L, (int)d, (int)Nr,
+                                              (int)Nc, (int)K, dt, dx, dWr, dWc, plan, ws,
+                                              (hipStream_t)stream);
+  return hip_status(e, "router backward launch");
+}
+
 omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
                                  int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
   if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");
@@ -181,6 +239,8 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_ROUTER: s = router_ws(L, d, Nr, Nc, K, dt, &need); break;
     case OMNI_OP_SCHEDULE: s = schedule_ws(L, K, N, B, &need); break;
     case OMNI_OP_EXPERT_FORWARD: s = expert_ws(L, d, N, K, dt, &need); break;
+    case OMNI_OP_EXPERT_BACKWARD: s = expert_bwd_ws(L, d, N, K, dt, &need); break;
+    case OMNI_OP_ROUTER_BACKWARD: s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

@@ -115,6 +115,13 @@ __device__ __forceinline__ float ord_float(unsigned int u) {
 // ----------------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments are pre-validated.
 
+// C[M, N] (+)= A[M, Kd] . B[N, Kd]^T on MFMA (bf16 in, fp32 out); B rows
+// n >= n_split come from B1 (row n - n_split), C rows m >= m_split go to C1.
+// Kd must be a multiple of 64.
+hipError_t launch_gemm_bt_bf16(const void* A, const void* B0, const void* B1, int n_split, int M,
+                               int N, int Kd, float* C0, float* C1, int m_split, int ldc,
+                               bool accumulate, hipStream_t s);
+
 // logits[L, Nr+Nc] (fp32) = x [L,d] . [Wr; Wc]^T
 hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int L, int d,
                               int Nr, int Nc, omni_dtype dt, float* logits, hipStream_t s);
@@ -131,6 +138,8 @@ struct SchedPlan {
   size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals;
 };
 SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
+// The sorted group ids left in the workspace by the last launch_schedule.
+const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
                            int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
 
@@ -145,5 +154,31 @@ hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const i
 // y[t] = sum_k act[t*K+k] * V[idx[t*K+k]]
 hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,
                              int K, omni_dtype dt, float* y, hipStream_t s);
+
+// ----------------------------------------------------------------- backward
+struct BwdPlan {
+  int M, U_max, ntiles;
+  SchedPlan sched;
+  size_t off_dh, off_ga, off_perm, off_eoff, off_seg, off_cnt, off_sched, ws_bytes;
+};
+BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K);
+// dx (expert part, overwritten), dgate, used experts and their dW / dV rows
+hipError_t launch_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
+                                  const float* gate, const float* dy, int L, int d, int N, int K,
+                                  omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
+                                  int32_t* n_uniq, float* dW_rows, float* dV_rows,
+                                  const BwdPlan& p, void* ws, hipStream_t s);
+
+struct RouterBwdPlan {
+  int Ntot_p, L_p;
+  size_t off_ds_hi, off_ds_lo, off_dsT_hi, off_dsT_lo, off_xT, off_wT, off_ds, ws_bytes;
+};
+RouterBwdPlan plan_router_backward(int64_t L, int64_t d, int64_t Nr, int64_t Nc, omni_dtype dt);
+// dx += router part; dWr, dWc overwritten
+hipError_t launch_router_backward(const void* x, const void* Wr, const void* Wc,
+                                  const int32_t* idx, const float* gate, const float* dgate,
+                                  int L, int d, int Nr, int Nc, int K, omni_dtype dt, float* dx,
+                                  float* dWr, float* dWc, const RouterBwdPlan& p, void* ws,
+                                  hipStream_t s);
 
 }  // namespace omni

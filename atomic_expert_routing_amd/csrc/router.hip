@@ -175,13 +175,21 @@ __device__ __forceinline__ int chunk_swz(int r) {
 // (b % 8) * per_xcd + b / 8 of the row-major tile order, so that each XCD
 // sweeps a contiguous band of output rows and the x and W panels its
 // concurrent workgroups share are fetched into its own L2 once.
+//
+// General form: C[M, N] = A[M, Kd] . B[N, Kd]^T (or C += when `accumulate`),
+// A and B bf16 row-major with Kd contiguous (Kd % BK == 0).  B rows n < n_split
+// come from B0, the others from B1 (the router stacks W_r over W_c); C rows
+// m < m_split go to C0, the others to C1 (row stride ldc), so that one product
+// can fill two separately owned matrices.
 template <int BK, int S, int NJ>
-__global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ Wr,
-                                                             const uint16_t* __restrict__ Wc,
-                                                             int L, int d, int Nr, int Nc,
-                                                             int tiles_n, int per_xcd,
-                                                             float* __restrict__ C) {
+__global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ B0,
+                                                         const uint16_t* __restrict__ B1,
+                                                         int M, int N, int Kd, int n_split,
+                                                         int tiles_n, int per_xcd,
+                                                         float* __restrict__ C0,
+                                                         float* __restrict__ C1, int m_split,
+                                                         int ldc, int accumulate) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
   constexpr int TN = 32 * NJ;             // tile columns
   constexpr int ROWB = 2 * BK;            // bytes per tile row
@@ -194,9 +202,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
   constexpr int LPWB = TILEB / 1024 / 4;  // and B
   static_assert(TILEB % 4096 == 0, "B tile must split into 1 KB loads over 4 waves");
   static_assert(S >= 2 && S <= 5, "pipeline depth");
-  const int Ntot = Nr + Nc;
   const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int tiles_m = (L + 127) / 128;
+  const int tiles_m = (M + 127) / 128;
   if (t >= tiles_m * tiles_n) return;  // whole workgroup, before any barrier
   const int tile_m = (t / tiles_n) * 128, tile_n = (t % tiles_n) * TN;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -210,14 +217,14 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
   for (int j = 0; j < LPWA; ++j) {
     const int r = (wave * LPWA + j) * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    asrc[j] = x + (size_t)min(tile_m + r, L - 1) * d + chunk * 8;
+    asrc[j] = A + (size_t)min(tile_m + r, M - 1) * Kd + chunk * 8;
   }
 #pragma unroll
   for (int j = 0; j < LPWB; ++j) {
     const int r = (wave * LPWB + j) * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    const int gn = min(tile_n + r, Ntot - 1);
-    bsrc[j] = (gn < Nr ? Wr + (size_t)gn * d : Wc + (size_t)(gn - Nr) * d) + chunk * 8;
+    const int gn = min(tile_n + r, N - 1);
+    bsrc[j] = (gn < n_split ? B0 + (size_t)gn * Kd : B1 + (size_t)(gn - n_split) * Kd) + chunk * 8;
   }
   auto issue = [&](int kt) {
     unsigned char* st = gsm + (kt % S) * STAGE;
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
     }
   };
 
-  const int nk = d / BK;
+  const int nk = Kd / BK;
   for (int kt = 0; kt < S - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt landed for this wave; after the barrier it has for every wave,
@@ -281,11 +288,14 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_pipe(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = tile_n + wn + j * 16 + (lane & 15);
-      if (col >= Ntot) continue;
+      if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = tile_m + wm + i * 16 + (lane >> 4) * 4 + r;
-        if (row < L) C[(size_t)row * Ntot + col] = acc[i][j][r];
+        if (row >= M) continue;
+        float* c = row < m_split ? C0 + (size_t)row * ldc + col
+                                 : C1 + (size_t)(row - m_split) * ldc + col;
+        *c = accumulate ? *c + acc[i][j][r] : acc[i][j][r];
       }
     }
 }
@@ -753,18 +763,26 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
 
 }  // namespace
 
+hipError_t launch_gemm_bt_bf16(const void* A, const void* B0, const void* B1, int n_split, int M,
+                               int N, int Kd, float* C0, float* C1, int m_split, int ldc,
+                               bool accumulate, hipStream_t s) {
+  constexpr int S = GEMM_STAGES, BK = GEMM_BK, NJ = GEMM_NJ;
+  if (Kd % BK != 0 || M <= 0 || N <= 0) return hipErrorInvalidValue;
+  const int tiles_n = (N + 32 * NJ - 1) / (32 * NJ);
+  const int tiles = ((M + 127) / 128) * tiles_n;
+  const int per_xcd = (tiles + 7) / 8;
+  const size_t lds = (size_t)S * (128 + 32 * NJ) * 2 * BK;
+  hipLaunchKernelGGL((gemm_bt_bf16_pipe<BK, S, NJ>), dim3(8 * per_xcd), dim3(256), lds, s,
+                     (const uint16_t*)A, (const uint16_t*)B0, (const uint16_t*)B1, M, N, Kd,
+                     n_split, tiles_n, per_xcd, C0, C1, m_split, ldc, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int L, int d,
                               int Nr, int Nc, omni_dtype dt, float* logits, hipStream_t s) {
   const int Ntot = Nr + Nc;
   if (dt == OMNI_BF16 && d % GEMM_BK == 0) {
-    constexpr int S = GEMM_STAGES, BK = GEMM_BK, NJ = GEMM_NJ;
-    const int tiles_n = (Ntot + 32 * NJ - 1) / (32 * NJ);
-    const int tiles = ((L + 127) / 128) * tiles_n;
-    const int per_xcd = (tiles + 7) / 8;
-    const size_t lds = (size_t)S * (128 + 32 * NJ) * 2 * BK;
-    hipLaunchKernelGGL((router_gemm_bf16_pipe<BK, S, NJ>), dim3(8 * per_xcd), dim3(256), lds, s,
-                       (const uint16_t*)x, (const uint16_t*)Wr, (const uint16_t*)Wc, L, d, Nr, Nc,
-                       tiles_n, per_xcd, logits);
+    return launch_gemm_bt_bf16(x, Wr, Wc, Nr, L, Ntot, d, logits, logits, L, Ntot, false, s);
   } else if (dt == OMNI_BF16) {  // d not a multiple of BK: zero-filled partial k-tile
     dim3 grid((Ntot + GBN - 1) / GBN, (L + GBM - 1) / GBM);
     hipLaunchKernelGGL(router_gemm_bf16, grid, dim3(256), 0, s, (const uint16_t*)x,

@@ -192,6 +192,11 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B) {
   return p;
 }
 
+const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws) {
+  const char* w = (const char*)ws;
+  return (const int32_t*)(w + (((plan.passes - 1) & 1) ? plan.off_keys_b : plan.off_keys_a));
+}
+
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
                            int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
   char* w = (char*)ws;

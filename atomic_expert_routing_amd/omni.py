@@ -16,14 +16,15 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 1
+_ABI_VERSION = 2
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
+OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD = 3, 4
 EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward",
-            "omni_expert_forward_token_centric", "omni_workspace_bytes", "omni_status_string",
-            "omni_last_error", "omni_abi_version")
+            "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
+            "omni_workspace_bytes", "omni_status_string", "omni_last_error", "omni_abi_version")
 
 
 class OmniError(RuntimeError):
@@ -53,10 +54,15 @@ def library() -> ctypes.CDLL:
                                         ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                       ctypes.c_int, vp, vp]
+    lib.omni_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                         ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.omni_router_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
     for f in ("omni_router", "omni_schedule", "omni_expert_forward",
-              "omni_expert_forward_token_centric", "omni_workspace_bytes"):
+              "omni_expert_forward_token_centric", "omni_expert_backward",
+              "omni_router_backward", "omni_workspace_bytes"):
         getattr(lib, f).restype = ctypes.c_int
     lib.omni_status_string.argtypes = [ctypes.c_int]
     lib.omni_status_string.restype = ctypes.c_char_p
@@ -199,6 +205,61 @@ def omni_expert_forward_token_centric(x, W, V, idx, gate, y=None, stream=None):
                                                        _stream(stream)),
            "omni_expert_forward_token_centric")
     return y
+
+
+def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None, n_uniq=None,
+                         dW_rows=None, dV_rows=None, ws=None, stream=None):
+    """Gradients of the expert assembly.
+
+    Returns (dx [L,d] f32 (expert part), dgate [L,K] f32, uniq [U_cap] int32,
+    n_uniq [1] int32, dW_rows [U_cap,d] f32, dV_rows [U_cap,d] f32) with
+    U_cap = min(N, L*K); only the first n_uniq entries / rows are defined.
+    """
+    L, d = x.shape
+    N = W.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    cap = min(N, L * K)
+    f32, i32 = torch.float32, torch.int32
+    kw = dict(device=x.device)
+    dx = torch.empty((L, d), dtype=f32, **kw) if dx is None else dx
+    dgate = torch.empty((L, K), dtype=f32, **kw) if dgate is None else dgate
+    uniq = torch.empty((cap,), dtype=i32, **kw) if uniq is None else uniq
+    n_uniq = torch.empty((1,), dtype=i32, **kw) if n_uniq is None else n_uniq
+    dW_rows = torch.empty((cap, d), dtype=f32, **kw) if dW_rows is None else dW_rows
+    dV_rows = torch.empty((cap, d), dtype=f32, **kw) if dV_rows is None else dV_rows
+    args = (_dev(x, "x"), _dev(W, "W", x.dtype, (N, d)), _dev(V, "V", x.dtype, (N, d)),
+            _dev(idx, "idx", i32, (L, K)), _dev(gate, "gate", f32, (L, K)),
+            _dev(dy, "dy", f32, (L, d)), L, d, N, K, dt, _dev(dx, "dx", f32, (L, d)),
+            _dev(dgate, "dgate", f32, (L, K)), _dev(uniq, "uniq", i32, (cap,)),
+            _dev(n_uniq, "n_uniq", i32, (1,)), _dev(dW_rows, "dW_rows", f32, (cap, d)),
+            _dev(dV_rows, "dV_rows", f32, (cap, d)))
+    need = omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_expert_backward(*args, pw, nw, _stream(stream)), "omni_expert_backward")
+    return dx, dgate, uniq, n_uniq, dW_rows, dV_rows
+
+
+def omni_router_backward(x, Wr, Wc, idx, gate, dgate, dx, dWr=None, dWc=None, ws=None,
+                         stream=None):
+    """Router gradients: adds the router part into dx (in place) and returns
+    (dx, dWr [N_r,d] f32, dWc [N_c,d] f32)."""
+    L, d = x.shape
+    Nr, Nc = Wr.shape[0], Wc.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    f32 = torch.float32
+    dWr = torch.empty((Nr, d), dtype=f32, device=x.device) if dWr is None else dWr
+    dWc = torch.empty((Nc, d), dtype=f32, device=x.device) if dWc is None else dWc
+    args = (_dev(x, "x"), _dev(Wr, "Wr", x.dtype, (Nr, d)), _dev(Wc, "Wc", x.dtype, (Nc, d)),
+            _dev(idx, "idx", torch.int32, (L, K)), _dev(gate, "gate", f32, (L, K)),
+            _dev(dgate, "dgate", f32, (L, K)), L, d, Nr, Nc, K, dt, _dev(dx, "dx", f32, (L, d)),
+            _dev(dWr, "dWr", f32, (Nr, d)), _dev(dWc, "dWc", f32, (Nc, d)))
+    need = omni_workspace_bytes(OMNI_OP_ROUTER_BACKWARD, L, d, Nr, Nc, K, Nr * Nc, 1, dt) \
+        if ws is None else 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_router_backward(*args, pw, nw, _stream(stream)), "omni_router_backward")
+    return dx, dWr, dWc
 
 
 class RoutedBranch:

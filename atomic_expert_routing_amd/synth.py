@@ -32,7 +32,7 @@ import numpy as np
 import torch
 
 ROWS_PER_BLOCK = 65536
-_TID = {"x": 0, "Wr": 1, "Wc": 2, "W": 3, "V": 4, "centres": 5, "cluster": 6}
+_TID = {"x": 0, "Wr": 1, "Wc": 2, "W": 3, "V": 4, "centres": 5, "cluster": 6, "dy": 7}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -140,6 +140,12 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
         W=normal_rows("W", w.N, w.d, std, seed, device, dt),
         V=normal_rows("V", w.N, w.d, std, seed, device, dt),
     )
+
+
+def upstream_grad(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """dy [L, d] fp32 ~ N(0, 1/d): the gradient arriving at the branch output
+    (a unit-variance loss gradient spread over d outputs)."""
+    return normal_rows("dy", w.L, w.d, 1.0 / math.sqrt(w.d), seed, device)
 
 
 def make_case(L, d, Nr, Nc, K, B, dtype="f32", seed=0, device="cpu",

@@ -8,6 +8,9 @@
  *   omni_schedule        expert-centric schedule: sorted tasks, group offsets
  *   omni_expert_forward  Dynamic Expert Assembly: y
  * and one comparison baseline, omni_expert_forward_token_centric.
+ * The backward of the branch runs in two more calls:
+ *   omni_expert_backward  dx (expert part), d gate, dW and dV of used experts
+ *   omni_router_backward  dW_r, dW_c, and the router part added into dx
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller, row-major and
@@ -38,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 1
+#define OMNI_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -59,7 +62,9 @@ typedef enum { OMNI_F32 = 0, OMNI_BF16 = 1 } omni_dtype;
 typedef enum {
   OMNI_OP_ROUTER = 0,
   OMNI_OP_SCHEDULE = 1,
-  OMNI_OP_EXPERT_FORWARD = 2
+  OMNI_OP_EXPERT_FORWARD = 2,
+  OMNI_OP_EXPERT_BACKWARD = 3,
+  OMNI_OP_ROUTER_BACKWARD = 4
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -161,6 +166,70 @@ OMNI_API omni_status omni_expert_forward_token_centric(const void* x, const void
                                                        const float* gate, int64_t L, int64_t d,
                                                        int64_t N, int64_t K, omni_dtype dt,
                                                        float* y, void* stream);
+
+/*
+ * omni_expert_backward - gradients of the expert assembly for an upstream
+ * gradient dy = dLoss/dy.
+ * Source: the chain rule of omni_expert_forward's definition (OmniMoE digest,
+ * method paragraph, steps 1 and 3: y_t = sum_k g_k sigma(x_t . w_k) v_k,
+ * sigma = SiLU).  Per task (t, k, e = idx[t,k]), h = x_t . W[e],
+ * u = V[e] . dy_t:
+ *   dgate[t,k] = SiLU(h) u
+ *   dh         = gate[t,k] u SiLU'(h),  SiLU'(h) = sig(h) (1 + h (1 - sig(h)))
+ *   dx_t       = sum_k dh W[e]                    (expert part only)
+ *   dW[e]      = sum over e's tasks of dh x_t
+ *   dV[e]      = sum over e's tasks of gate SiLU(h) dy_t
+ *
+ *   x, W, V, idx, gate   as for omni_expert_forward (the forward's routing)
+ *   dy      [L, d]  fp32      upstream gradient
+ *   dx      [L, d]  fp32 out  expert part of dLoss/dx, fully overwritten
+ *   dgate   [L, K]  fp32 out  dLoss/dgate, fully overwritten
+ *   uniq    [U_cap] int32 out the experts that have tasks, ascending
+ *   n_uniq  [1]     int32 out U, the number of entries of uniq
+ *   dW_rows [U_cap, d] fp32 out  row r = dLoss/dW[uniq[r]] for r < U
+ *   dV_rows [U_cap, d] fp32 out  row r = dLoss/dV[uniq[r]] for r < U
+ * with U_cap = min(N, L*K); rows and entries at or past U are left as they
+ * were.  Experts without tasks have zero gradient and no row (a sparse row
+ * gradient: dense fp32 dW and dV would be 2*N*d*4 bytes).  Each row is summed
+ * by one workgroup over the expert's tasks in (token, k) order, so the
+ * result is deterministic.  Same size limits as omni_expert_forward.
+ * Workspace: per-task terms, the tasks sorted by expert id and the
+ * per-expert segment table (omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD)).
+ */
+OMNI_API omni_status omni_expert_backward(const void* x, const void* W, const void* V,
+                                          const int32_t* idx, const float* gate, const float* dy,
+                                          int64_t L, int64_t d, int64_t N, int64_t K,
+                                          omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
+                                          int32_t* n_uniq, float* dW_rows, float* dV_rows,
+                                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_router_backward - gradients of the Cartesian Product Router.
+ * Source: the chain rule of omni_router's definition (OmniMoE digest,
+ * method paragraph, step 2: s = x W^T, p = LogSoftmax(s), S_ij = p_r[i] +
+ * p_c[j], gate = softmax over the K selected S).  The top-K selection is
+ * piecewise constant and passes no gradient.  Per token:
+ *   dS_k    = gate_k (dgate_k - sum_j gate_j dgate_j)
+ *   ds_r[i] = sum of dS_k over the selected ids in grid row i (n = i*N_c + j),
+ *   ds_c[j] likewise over grid column j; the LogSoftmax Jacobian's other term,
+ *   -softmax(s) * sum_k dS_k, is zero because sum_k dS_k = 0
+ *   dW_r = ds_r^T x,  dW_c = ds_c^T x,  dx += ds_r W_r + ds_c W_c
+ *
+ *   x, Wr, Wc, idx, gate   as for omni_router (idx, gate: its outputs)
+ *   dgate   [L, K]  fp32      dLoss/dgate (e.g. from omni_expert_backward)
+ *   dx      [L, d]  fp32 in/out  the router part is ADDED to it
+ *   dWr     [N_r, d], dWc [N_c, d]  fp32 out, fully overwritten
+ * bf16 inputs: ds is split into two bf16 terms (high part and remainder,
+ * about 16 significant bits) for the MFMA products, accumulated in fp32.
+ * Same size limits as omni_router.  Workspace: the logit gradients and
+ * transposed operands (omni_workspace_bytes(OMNI_OP_ROUTER_BACKWARD)).
+ */
+OMNI_API omni_status omni_router_backward(const void* x, const void* Wr, const void* Wc,
+                                          const int32_t* idx, const float* gate,
+                                          const float* dgate, int64_t L, int64_t d, int64_t Nr,
+                                          int64_t Nc, int64_t K, omni_dtype dt, float* dx,
+                                          float* dWr, float* dWc, void* ws, size_t ws_bytes,
+                                          void* stream);
 
 /*
  * omni_workspace_bytes - workspace size needed by one call of `op` with

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 1
+    assert lib.omni_abi_version() == 2
 
 
 def test_status_strings():
@@ -125,6 +125,34 @@ def test_calls_reject_before_launch():
     s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 5, omni.OMNI_F32, fake, fake, fake,
                         fake, 1 << 20, None)
     assert s == omni.OMNI_ERR_INVALID_ARG and b"K" in lib.omni_last_error()
+
+
+def test_backward_workspace_sizes_and_validation():
+    # expert backward: per-task terms, expert-sorted tasks, per-expert segments
+    ws = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L=4096, d=2048, K=128,
+                                   N=1700416)
+    M = 4096 * 128
+    assert ws >= (4 * M + 1700416) * 4 and ws < (12 * M + 1700416 + 4096) * 4
+    # router backward (bf16): hi/lo logit gradients, their transposes, x^T, W_rc^T
+    ws = omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER_BACKWARD, L=4096, d=2048, Nr=1304,
+                                   Nc=1304, K=128)
+    assert ws == (2 * 4096 * 2624 * 2 + 2 * 2608 * 4096 * 2 + 2048 * 4096 * 2
+                  + 2048 * 2624 * 2)
+    # fp32: one fp32 logit-gradient matrix
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER_BACKWARD, L=64, d=64, Nr=32, Nc=32,
+                                     K=16, dtype=omni.OMNI_F32) == 64 * 64 * 4
+    for op in (omni.OMNI_OP_EXPERT_BACKWARD, omni.OMNI_OP_ROUTER_BACKWARD):
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(op, L=4, d=12, Nr=4, Nc=4, K=2, N=16)
+        assert e.value.status == omni.OMNI_ERR_UNSUPPORTED
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)
+    s = lib.omni_expert_backward(fake, fake, fake, fake, fake, fake, 4, 8, 16, 2, omni.OMNI_BF16,
+                                 fake, fake, fake, None, fake, fake, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
+    s = lib.omni_router_backward(fake, fake, fake, fake, fake, fake, 4, 8, 2, 2, 2, omni.OMNI_BF16,
+                                 fake, fake, fake, fake, 16, None)
+    assert s == omni.OMNI_ERR_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors():
