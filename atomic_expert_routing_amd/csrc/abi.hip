@@ -190,8 +190,9 @@ omni_status omni_expert_forward_token_centric(const void* x, const void* W, cons
 omni_status omni_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
                                  const float* gate, const float* dy, int64_t L, int64_t d,
                                  int64_t N, int64_t K, omni_dtype dt, float* dx, float* dgate,
-                                 int32_t* uniq, int32_t* n_uniq, float* dW_rows, float* dV_rows,
-                                 void* ws, size_t ws_bytes, void* stream) {
+                                 int32_t* uniq, int32_t* n_uniq, omni_dtype grad_dt,
+                                 void* dW_rows, void* dV_rows, void* ws, size_t ws_bytes,
+                                 void* stream) {
   size_t need = 0;
   omni_status s = expert_bwd_ws(L, d, N, K, dt, &need);
   if (s != OMNI_OK) return s;
@@ -202,11 +203,13 @@ omni_status omni_expert_backward(const void* x, const void* W, const void* V, co
       !aligned16(dW_rows) || !aligned16(dV_rows))
     return fail(OMNI_ERR_INVALID_ARG,
                 "omni_expert_backward: x, W, V, dy, dx, dW_rows and dV_rows must be 16-byte aligned");
+  if (grad_dt != OMNI_F32 && grad_dt != OMNI_BF16)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_backward: unknown grad_dt %d", (int)grad_dt);
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
   const omni::BwdPlan plan = omni::plan_expert_backward(L, d, N, K);
   hipError_t e = omni::launch_expert_backward(x, W, V, idx, gate, dy, (int)L, (int)d, (int)N,
-                                              (int)K, dt, dx, dgate, uniq, n_uniq, dW_rows,
-                                              dV_rows, plan, ws, (hipStream_t)stream);
+                                              (int)K, dt, dx, dgate, uniq, n_uniq, grad_dt,
+                                              dW_rows, dV_rows, plan, ws, (hipStream_t)stream);
   return hip_status(e, "expert backward launch");
 }
 

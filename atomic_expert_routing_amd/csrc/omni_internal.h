@@ -166,8 +166,8 @@ BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K);
 hipError_t launch_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
                                   const float* gate, const float* dy, int L, int d, int N, int K,
                                   omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
-                                  int32_t* n_uniq, float* dW_rows, float* dV_rows,
-                                  const BwdPlan& p, void* ws, hipStream_t s);
+                                  int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
+                                  void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s);
 
 struct RouterBwdPlan {
   int Ntot_p, L_p;

@@ -55,7 +55,8 @@ def library() -> ctypes.CDLL:
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                       ctypes.c_int, vp, vp]
     lib.omni_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
-                                         ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+                                         ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                         vp, sz, vp]
     lib.omni_router_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
@@ -208,12 +209,14 @@ def omni_expert_forward_token_centric(x, W, V, idx, gate, y=None, stream=None):
 
 
 def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None, n_uniq=None,
-                         dW_rows=None, dV_rows=None, ws=None, stream=None):
+                         dW_rows=None, dV_rows=None, ws=None, stream=None,
+                         grad_dtype=torch.float32):
     """Gradients of the expert assembly.
 
     Returns (dx [L,d] f32 (expert part), dgate [L,K] f32, uniq [U_cap] int32,
-    n_uniq [1] int32, dW_rows [U_cap,d] f32, dV_rows [U_cap,d] f32) with
+    n_uniq [1] int32, dW_rows [U_cap,d], dV_rows [U_cap,d]) with
     U_cap = min(N, L*K); only the first n_uniq entries / rows are defined.
+    The gradient rows are float32 or bfloat16 (grad_dtype).
     """
     L, d = x.shape
     N = W.shape[0]
@@ -226,14 +229,15 @@ def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None,
     dgate = torch.empty((L, K), dtype=f32, **kw) if dgate is None else dgate
     uniq = torch.empty((cap,), dtype=i32, **kw) if uniq is None else uniq
     n_uniq = torch.empty((1,), dtype=i32, **kw) if n_uniq is None else n_uniq
-    dW_rows = torch.empty((cap, d), dtype=f32, **kw) if dW_rows is None else dW_rows
-    dV_rows = torch.empty((cap, d), dtype=f32, **kw) if dV_rows is None else dV_rows
+    gdt = dW_rows.dtype if dW_rows is not None else grad_dtype
+    dW_rows = torch.empty((cap, d), dtype=gdt, **kw) if dW_rows is None else dW_rows
+    dV_rows = torch.empty((cap, d), dtype=gdt, **kw) if dV_rows is None else dV_rows
     args = (_dev(x, "x"), _dev(W, "W", x.dtype, (N, d)), _dev(V, "V", x.dtype, (N, d)),
             _dev(idx, "idx", i32, (L, K)), _dev(gate, "gate", f32, (L, K)),
             _dev(dy, "dy", f32, (L, d)), L, d, N, K, dt, _dev(dx, "dx", f32, (L, d)),
             _dev(dgate, "dgate", f32, (L, K)), _dev(uniq, "uniq", i32, (cap,)),
-            _dev(n_uniq, "n_uniq", i32, (1,)), _dev(dW_rows, "dW_rows", f32, (cap, d)),
-            _dev(dV_rows, "dV_rows", f32, (cap, d)))
+            _dev(n_uniq, "n_uniq", i32, (1,)), _dtype_code(dW_rows),
+            _dev(dW_rows, "dW_rows", gdt, (cap, d)), _dev(dV_rows, "dV_rows", gdt, (cap, d)))
     need = omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
     pw, nw = _workspace(ws, need, x.device)
     _check(library().omni_expert_backward(*args, pw, nw, _stream(stream)), "omni_expert_backward")

@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MB "
                          "Infinity Cache, timed with events (0 to skip)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward calls")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB "
                          "(reference kernel for scaling hardware byte counters)")
@@ -134,6 +136,82 @@ def cpu_baseline(inp, w, n_tok, seed):
                    f"host affinity {len(os.sched_getaffinity(0))} cpus; W/V rows and router "
                    f"weights copied to host before timing"),
         "stages_s": {"route": round(t_route, 3), "schedule+assembly": round(t_rest, 3)},
+    }
+
+
+def time_backward(inp, w, br, steps, seed):
+    """omni_expert_backward + omni_router_backward on the step's routing, for a
+    seeded upstream gradient; preallocated outputs and workspaces.  The expert
+    backward is timed with fp32 and with bf16 gradient rows."""
+    import torch
+
+    from atomic_expert_routing_amd import omni, synth
+
+    dy = synth.upstream_grad(w, seed=seed, device="cuda")
+    L, d, K, N = w.L, w.d, w.K, w.N
+    cap = min(N, L * K)
+    f32, i32 = torch.float32, torch.int32
+    dx = torch.empty((L, d), dtype=f32, device="cuda")
+    dgate = torch.empty((L, K), dtype=f32, device="cuda")
+    uniq = torch.empty((cap,), dtype=i32, device="cuda")
+    n_uniq = torch.empty((1,), dtype=i32, device="cuda")
+    dW = torch.empty((cap, d), dtype=f32, device="cuda")
+    dV = torch.empty((cap, d), dtype=f32, device="cuda")
+    dW16 = torch.empty((cap, d), dtype=torch.bfloat16, device="cuda")
+    dV16 = torch.empty((cap, d), dtype=torch.bfloat16, device="cuda")
+    dWr = torch.empty((w.Nr, d), dtype=f32, device="cuda")
+    dWc = torch.empty((w.Nc, d), dtype=f32, device="cuda")
+    dt = omni.OMNI_BF16 if w.dtype == "bf16" else omni.OMNI_F32
+    ws_e = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L, d, 1, 1, K, N,
+                                                 1, dt), dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER_BACKWARD, L, d, w.Nr, w.Nc,
+                                                 K, N, 1, dt), dtype=torch.uint8, device="cuda")
+
+    def run(ev=None, rows=(dW, dV)):
+        if ev is not None:
+            ev[0].record()
+        omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy, dx, dgate,
+                                  uniq, n_uniq, rows[0], rows[1], ws_e)
+        if ev is not None:
+            ev[1].record()
+        omni.omni_router_backward(inp["x"], inp["Wr"], inp["Wc"], br.idx, br.gate, dgate, dx,
+                                  dWr, dWc, ws_r)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    exp_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    rt_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
+    evs16 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    run(rows=(dW16, dV16))
+    for e in evs16:
+        run(e, rows=(dW16, dV16))
+    torch.cuda.synchronize()
+    exp16_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs16)
+    U = int(n_uniq.item())
+    es = 2 if w.dtype == "bf16" else 4
+    # unique W and V rows read, their fp32 dW and dV rows written; x and dy
+    # read, dx written; dgate written and 12 B of task metadata per task
+    exp_bytes = 2 * U * d * es + 2 * U * d * 4 + L * d * es + 2 * L * d * 4 + w.M * (4 + 12)
+    router_flops = 2 * 2.0 * L * d * (w.Nr + w.Nc)  # ds^T x and ds W_rc
+    exp16_bytes = exp_bytes - 2 * U * d * 2
+    return {
+        "expert_backward_ms": round(exp_ms, 4),
+        "expert_backward_bf16_rows_ms": round(exp16_ms, 4),
+        "expert_backward_bf16_rows_hbm_frac": round(
+            exp16_bytes / (exp16_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "router_backward_ms": round(rt_ms, 4),
+        "unique_experts": U,
+        "expert_backward_algorithmic_bytes": exp_bytes,
+        "expert_backward_hbm_frac": round(exp_bytes / (exp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "router_backward_tflops": round(router_flops / (rt_ms * 1e-3) / 1e12, 1),
+        "note": "router products run twice (bf16 high and low parts of the logit gradients)",
     }
 
 
@@ -279,6 +357,9 @@ def main():
     tc_ms = statistics.median(tc_times)
     out["token_centric_assembly_ms"] = round(tc_ms, 4)
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
+
+    if not args.no_backward:
+        out["backward"] = time_backward(inp, w, br, args.steps, args.seed)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")

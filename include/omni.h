@@ -186,13 +186,16 @@ OMNI_API omni_status omni_expert_forward_token_centric(const void* x, const void
  *   dgate   [L, K]  fp32 out  dLoss/dgate, fully overwritten
  *   uniq    [U_cap] int32 out the experts that have tasks, ascending
  *   n_uniq  [1]     int32 out U, the number of entries of uniq
- *   dW_rows [U_cap, d] fp32 out  row r = dLoss/dW[uniq[r]] for r < U
- *   dV_rows [U_cap, d] fp32 out  row r = dLoss/dV[uniq[r]] for r < U
+ *   grad_dt          dtype of the two gradient-row arrays (OMNI_F32, or
+ *                    OMNI_BF16: the fp32 sums rounded to nearest even)
+ *   dW_rows [U_cap, d] grad_dt out  row r = dLoss/dW[uniq[r]] for r < U
+ *   dV_rows [U_cap, d] grad_dt out  row r = dLoss/dV[uniq[r]] for r < U
  * with U_cap = min(N, L*K); rows and entries at or past U are left as they
  * were.  Experts without tasks have zero gradient and no row (a sparse row
  * gradient: dense fp32 dW and dV would be 2*N*d*4 bytes).  Each row is summed
  * by one workgroup over the expert's tasks in (token, k) order, so the
- * result is deterministic.  Same size limits as omni_expert_forward.
+ * result is deterministic.  Writing the rows is most of this call's memory
+ * traffic; bf16 rows halve it.  Same size limits as omni_expert_forward.
  * Workspace: per-task terms, the tasks sorted by expert id and the
  * per-expert segment table (omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD)).
  */
@@ -200,8 +203,9 @@ OMNI_API omni_status omni_expert_backward(const void* x, const void* W, const vo
                                           const int32_t* idx, const float* gate, const float* dy,
                                           int64_t L, int64_t d, int64_t N, int64_t K,
                                           omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
-                                          int32_t* n_uniq, float* dW_rows, float* dV_rows,
-                                          void* ws, size_t ws_bytes, void* stream);
+                                          int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
+                                          void* dV_rows, void* ws, size_t ws_bytes,
+                                          void* stream);
 
 /*
  * omni_router_backward - gradients of the Cartesian Product Router.

@@ -148,7 +148,8 @@ def test_backward_workspace_sizes_and_validation():
     lib = omni.library()
     fake = ctypes.c_void_p(4096)
     s = lib.omni_expert_backward(fake, fake, fake, fake, fake, fake, 4, 8, 16, 2, omni.OMNI_BF16,
-                                 fake, fake, fake, None, fake, fake, fake, 1 << 20, None)
+                                 fake, fake, fake, None, omni.OMNI_F32, fake, fake, fake, 1 << 20,
+                                 None)
     assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
     s = lib.omni_router_backward(fake, fake, fake, fake, fake, fake, 4, 8, 2, 2, 2, omni.OMNI_BF16,
                                  fake, fake, fake, fake, 16, None)

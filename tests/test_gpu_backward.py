@@ -37,8 +37,9 @@ def need_gpu():
     omni.library()
 
 
-def gpu_backward(inp, idx, gate, dy):
-    out = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], idx, gate, dy)
+def gpu_backward(inp, idx, gate, dy, grad_dtype=torch.float32):
+    out = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], idx, gate, dy,
+                                    grad_dtype=grad_dtype)
     dx, dgate, uniq, n_uniq, dW, dV = out
     dx_total = dx.clone()
     _, dWr, dWc = omni.omni_router_backward(inp["x"], inp["Wr"], inp["Wc"], idx, gate, dgate,
@@ -99,6 +100,13 @@ def test_backward_matches_oracle(case):
         errs["dWc"] = check_y(g["dWc"], dWc_o, RTOL_ROUTER)
         errs["dx"] = check_y(g["dx_total"], to_np(g["dx"]).astype(np.float64) + dxr_o, RTOL_ROUTER)
     say("  " + " ".join(f"{k}={v[0]:.1e}" for k, v in errs.items()))
+    # bf16 gradient rows: the same fp32 sums rounded to nearest even
+    b = gpu_backward(inp, idx, gate, dy, grad_dtype=torch.bfloat16)
+    n = g["n"]
+    assert b["n"] == n and b["dW"].dtype == torch.bfloat16
+    assert torch.equal(b["dW"][:n], g["dW"][:n].to(torch.bfloat16))
+    assert torch.equal(b["dV"][:n], g["dV"][:n].to(torch.bfloat16))
+    assert torch.equal(b["dx"], g["dx"]) and torch.equal(b["dgate"], g["dgate"])
 
 
 def test_backward_is_deterministic():
