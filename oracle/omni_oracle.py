@@ -37,7 +37,8 @@ design notes of the repository):
 * group of expert e is floor(e / B) (B consecutive expert ids); the schedule
   is the task ids sorted by (group, token, task id).
 * y starts at zero and receives every task's contribution (no bias, no
-  capacity limit, no shared MLP: the routed branch only).
+  capacity limit); the shared dense MLP is a separate branch (shared_mlp),
+  read as a SwiGLU block, and layer_forward adds the two.
 
 Pinned by the CPU tests (tests/test_oracle_*.py) against brute force, closed
 forms and invariants; no function here is "parity unpinned".
@@ -285,3 +286,28 @@ def routed_forward(x, Wr, Wc, W, V, K, B):
     y = assemble_expert_centric(x, W, V, idx, gate, perm, group_off)
     return dict(idx=idx, score=score, gate=gate, perm=perm,
                 group_off=group_off, y=y)
+
+
+# ---------------------------------------------------------------------------
+# Shared dense MLP and the whole layer  [digest, step 1: y = ... + MLP(x);
+# resume-de 2.1: a standard dense MLP branch active for every input]
+# ---------------------------------------------------------------------------
+
+def shared_mlp(x, Wg, Wu, Wd):
+    """MLP(x) = (SiLU(x W_g^T) * (x W_u^T)) W_d^T, a SwiGLU feed-forward block.
+
+    The pages name the branch and its role but not its shape; the digest's
+    "SwiGLU" remark has no gate vector to act on in an atomic expert and is
+    read as describing this branch.  Wg, Wu [d_ff, d]; Wd [d, d_ff] (one row
+    per output, the layout of a linear layer's weight).
+    """
+    x, Wg, Wu, Wd = as_f64(x), as_f64(Wg), as_f64(Wu), as_f64(Wd)
+    return (silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+
+
+def layer_forward(x, Wr, Wc, W, V, K, B, Wg, Wu, Wd):
+    """The whole layer: routed branch plus the shared dense MLP."""
+    out = routed_forward(x, Wr, Wc, W, V, K, B)
+    out["mlp"] = shared_mlp(x, Wg, Wu, Wd)
+    out["layer"] = out["y"] + out["mlp"]
+    return out
