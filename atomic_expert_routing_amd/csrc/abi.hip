@@ -103,6 +103,21 @@ omni_status router_bwd_ws(int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t 
   return OMNI_OK;
 }
 
+omni_status mlp_ws(int64_t L, int64_t d, int64_t F, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = check_dtype_d(dt, d)) != OMNI_OK) return s;
+  if (L <= 0 || F <= 0)
+    return fail(OMNI_ERR_INVALID_ARG, "L and d_ff must be positive (L=%lld d_ff=%lld)", (long long)L,
+                (long long)F);
+  if (L > I32_LIMIT / F || L > I32_LIMIT / d)
+    return fail(OMNI_ERR_UNSUPPORTED, "L*d_ff or L*d exceeds 2^31-1");
+  if (dt == OMNI_BF16 && (d % omni::GEMM_KTILE || F % omni::GEMM_KTILE))
+    return fail(OMNI_ERR_UNSUPPORTED, "bf16 shared MLP needs d and d_ff multiples of %d (d=%lld d_ff=%lld)",
+                omni::GEMM_KTILE, (long long)d, (long long)F);
+  *out = omni::shared_mlp_ws_bytes(L, F, dt);
+  return OMNI_OK;
+}
+
 omni_status check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
     return fail(OMNI_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
@@ -233,6 +248,21 @@ omni_status omni_router_backward(const void* x, const void* Wr, const void* Wc,
   return hip_status(e, "router backward launch");
 }
 
+omni_status omni_shared_mlp(const void* x, const void* Wg, const void* Wu, const void* Wd, int64_t L,
+                            int64_t d, int64_t d_ff, omni_dtype dt, float* y, int accumulate,
+                            void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = mlp_ws(L, d, d_ff, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !Wg || !Wu || !Wd || !y) return fail(OMNI_ERR_INVALID_ARG, "omni_shared_mlp: NULL array pointer");
+  if (!aligned16(x) || !aligned16(Wg) || !aligned16(Wu) || !aligned16(Wd) || !aligned16(y))
+    return fail(OMNI_ERR_INVALID_ARG, "omni_shared_mlp: x, Wg, Wu, Wd and y must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  hipError_t e = omni::launch_shared_mlp(x, Wg, Wu, Wd, (int)L, (int)d, (int)d_ff, dt, y,
+                                         accumulate != 0, ws, (hipStream_t)stream);
+  return hip_status(e, "shared MLP launch");
+}
+
 omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
                                  int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
   if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");
@@ -244,6 +274,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_EXPERT_FORWARD: s = expert_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_EXPERT_BACKWARD: s = expert_bwd_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_ROUTER_BACKWARD: s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need); break;
+    case OMNI_OP_SHARED_MLP: s = mlp_ws(L, d, N, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

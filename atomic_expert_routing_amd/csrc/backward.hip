@@ -428,65 +428,6 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
   }
 }
 
-// ------------------------------------------------------------------ fp32 product
-// C[m, n] (+)= sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk], 64 x 64 tiles.
-constexpr int GF = 64, GFK = 16;
-
-__global__ __launch_bounds__(256) void gemm_f32_strided(const float* __restrict__ A, long sam,
-                                                        long sak, const float* __restrict__ B,
-                                                        long sbn, long sbk, int M, int N, int Kd,
-                                                        float* __restrict__ C, int ldc,
-                                                        int accumulate) {
-  __shared__ float As[GFK][GF + 1];
-  __shared__ float Bs[GFK][GF + 1];
-  const int tile_m = blockIdx.y * GF, tile_n = blockIdx.x * GF;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kd; k0 += GFK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c % GF, k = c / GF;  // r fastest: m/n-contiguous reads
-      const int gm = tile_m + r, gn = tile_n + r, gk = k0 + k;
-      As[k][r] = (gm < M && gk < Kd) ? A[gm * sam + gk * sak] : 0.f;
-      Bs[k][r] = (gn < N && gk < Kd) ? B[gn * sbn + gk * sbk] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < GFK; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = tile_m + ty * 4 + i;
-    if (row >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = tile_n + tx * 4 + j;
-      if (col >= N) continue;
-      float* c = C + (size_t)row * ldc + col;
-      *c = accumulate ? *c + acc[i][j] : acc[i][j];
-    }
-  }
-}
-
-hipError_t gemm_f32(const float* A, long sam, long sak, const float* B, long sbn, long sbk, int M,
-                    int N, int Kd, float* C, int ldc, bool accumulate, hipStream_t s) {
-  const dim3 grid((N + GF - 1) / GF, (M + GF - 1) / GF);
-  hipLaunchKernelGGL(gemm_f32_strided, grid, dim3(256), 0, s, A, sam, sak, B, sbn, sbk, M, N, Kd,
-                     C, ldc, accumulate ? 1 : 0);
-  return hipGetLastError();
-}
-
 template <bool BF16>
 hipError_t launch_bwd_token_t(const void* x, const void* W, const void* V, const int32_t* idx,
                               const float* gate, const float* dy, int L, int d, int K, float* dx,

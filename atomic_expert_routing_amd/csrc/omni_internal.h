@@ -115,12 +115,30 @@ __device__ __forceinline__ float ord_float(unsigned int u) {
 // ----------------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments are pre-validated.
 
+// k-tile depth of the pipelined MFMA product: its Kd must be a multiple
+constexpr int GEMM_KTILE = 64;
+
 // C[M, N] (+)= A[M, Kd] . B[N, Kd]^T on MFMA (bf16 in, fp32 out); B rows
 // n >= n_split come from B1 (row n - n_split), C rows m >= m_split go to C1.
 // Kd must be a multiple of 64.
 hipError_t launch_gemm_bt_bf16(const void* A, const void* B0, const void* B1, int n_split, int M,
                                int N, int Kd, float* C0, float* C1, int m_split, int ldc,
                                bool accumulate, hipStream_t s);
+
+// out[M, F] (bf16) = SiLU(A Wg^T) * (A Wu^T), A [M, Kd], Wg and Wu [F, Kd] bf16;
+// F % 16 == 0, Kd % GEMM_KTILE == 0
+hipError_t launch_gemm_swiglu_bf16(const void* A, const void* Wg, const void* Wu, int M, int F,
+                                   int Kd, uint16_t* out, hipStream_t s);
+
+// fp32 VALU product C[m, n] (+)= sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk]
+hipError_t gemm_f32(const float* A, long sam, long sak, const float* B, long sbn, long sbk, int M,
+                    int N, int Kd, float* C, int ldc, bool accumulate, hipStream_t s);
+
+// y (+)= SiLU(x Wg^T) * (x Wu^T) Wd^T; ws per shared_mlp_ws_bytes
+size_t shared_mlp_ws_bytes(int64_t L, int64_t F, omni_dtype dt);
+hipError_t launch_shared_mlp(const void* x, const void* Wg, const void* Wu, const void* Wd, int L,
+                             int d, int F, omni_dtype dt, float* y, bool accumulate, void* ws,
+                             hipStream_t s);
 
 // logits[L, Nr+Nc] (fp32) = x [L,d] . [Wr; Wc]^T
 hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int L, int d,

@@ -4,8 +4,10 @@
 // logits s_r = x W_r, s_c = x W_c, LogSoftmax to p_r and p_c, scores
 // S_ij = p_r[i] + p_c[j] on the implicit N_r x N_c grid, global top-K.
 //
-// Two kernels:
-//   router_gemm_*    logits[L, N_r+N_c] = x . [W_r; W_c]^T   (bf16: MFMA)
+// Kernels:
+//   the logits logits[L, N_r+N_c] = x . [W_r; W_c]^T: bf16 on the pipelined
+//                    MFMA product of gemm.hip when d % 64 == 0, else
+//                    router_gemm_bf16 (register-staged MFMA); fp32 on VALU
 //   router_topk      one workgroup per token: LogSoftmax, row/column
 //                    pre-selection, K x K candidate merge, gate softmax.
 
@@ -118,194 +120,6 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t* __restri
       }
     }
 }
-
-// ------------------------------------------------------------------ bf16 GEMM, pipelined
-// The same 128 x 128 tile and wave layout, with the k-tiles (BK deep)
-// streamed through S LDS stages by direct global->LDS loads
-// (global_load_lds_dwordx4: each instruction writes 64 lanes x 16 bytes of
-// LDS without register staging), so S-1 k-tiles are in flight while one is
-// multiplied.  A stage holds the A and B tiles as 128 rows x 2*BK bytes; the
-// 16-byte chunk c of row r sits in slot c ^ swz(r), which spreads the 16
-// rows read by one ds_read_b128 over 16 distinct bank groups.  Rows past L
-// or N_r+N_c are loaded from a clamped row (their results are never
-// stored).  Needs d % BK == 0 (no partial k-tile).
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most n loads of this wave are outstanding (n a multiple of
-// the loads per k-tile: 4 or 8).
-template <int N>
-__device__ __forceinline__ void wait_vm_imm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most i * N of this wave's vector loads are outstanding
-// (i = 0 .. MAXI, the k-tiles allowed to stay in flight; N loads per k-tile).
-template <int N, int MAXI>
-__device__ __forceinline__ void wait_vm_tiles(int i) {
-  if constexpr (MAXI >= 3) {
-    if (i >= 3) return wait_vm_imm<3 * N>();
-  }
-  if constexpr (MAXI >= 2) {
-    if (i >= 2) return wait_vm_imm<2 * N>();
-  }
-  if constexpr (MAXI >= 1) {
-    if (i >= 1) return wait_vm_imm<N>();
-  }
-  wait_vm_imm<0>();
-}
-
-// Workgroup barrier without the fence of __syncthreads (which would also
-// wait for every direct-to-LDS load still in flight).
-__device__ __forceinline__ void block_sync_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int BK>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (BK == 64) return (r >> 1) & 7;  // 8 chunks per 128-byte row
-  else return (r >> 2) & 3;                     // 4 chunks per 64-byte row
-}
-
-// Tiles are 128 x (32 NJ): 4 waves as 2 x 2, each 64 x 16 NJ outputs held as
-// 4 x NJ MFMA 16x16 accumulators.  The grid is one-dimensional and the tile
-// order is XCD-aware: workgroup b runs on XCD b % 8 and takes tile
-// (b % 8) * per_xcd + b / 8 of the row-major tile order, so that each XCD
-// sweeps a contiguous band of output rows and the x and W panels its
-// concurrent workgroups share are fetched into its own L2 once.
-//
-// General form: C[M, N] = A[M, Kd] . B[N, Kd]^T (or C += when `accumulate`),
-// A and B bf16 row-major with Kd contiguous (Kd % BK == 0).  B rows n < n_split
-// come from B0, the others from B1 (the router stacks W_r over W_c); C rows
-// m < m_split go to C0, the others to C1 (row stride ldc), so that one product
-// can fill two separately owned matrices.
-template <int BK, int S, int NJ>
-__global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ B0,
-                                                         const uint16_t* __restrict__ B1,
-                                                         int M, int N, int Kd, int n_split,
-                                                         int tiles_n, int per_xcd,
-                                                         float* __restrict__ C0,
-                                                         float* __restrict__ C1, int m_split,
-                                                         int ldc, int accumulate) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
-  constexpr int TN = 32 * NJ;             // tile columns
-  constexpr int ROWB = 2 * BK;            // bytes per tile row
-  constexpr int TILEA = 128 * ROWB;       // bytes of the A tile
-  constexpr int TILEB = TN * ROWB;        // bytes of the B tile
-  constexpr int STAGE = TILEA + TILEB;
-  constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;           // rows per 1 KB load instruction
-  constexpr int LPWA = TILEA / 1024 / 4;  // loads per wave per k-tile, A
-  constexpr int LPWB = TILEB / 1024 / 4;  // and B
-  static_assert(TILEB % 4096 == 0, "B tile must split into 1 KB loads over 4 waves");
-  static_assert(S >= 2 && S <= 5, "pipeline depth");
-  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int tiles_m = (M + 127) / 128;
-  if (t >= tiles_m * tiles_n) return;  // whole workgroup, before any barrier
-  const int tile_m = (t / tiles_n) * 128, tile_n = (t % tiles_n) * TN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (16 * NJ);
-
-  // load j of wave w fills bytes [(LPW*w + j) * 1024, +1024) of a tile
-  const uint16_t* asrc[LPWA];
-  const uint16_t* bsrc[LPWB];
-#pragma unroll
-  for (int j = 0; j < LPWA; ++j) {
-    const int r = (wave * LPWA + j) * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    asrc[j] = A + (size_t)min(tile_m + r, M - 1) * Kd + chunk * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < LPWB; ++j) {
-    const int r = (wave * LPWB + j) * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    const int gn = min(tile_n + r, N - 1);
-    bsrc[j] = (gn < n_split ? B0 + (size_t)gn * Kd : B1 + (size_t)(gn - n_split) * Kd) + chunk * 8;
-  }
-  auto issue = [&](int kt) {
-    unsigned char* st = gsm + (kt % S) * STAGE;
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < LPWA; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[j] + k0),
-                                       (lds_void*)(st + (wave * LPWA + j) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < LPWB; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + k0),
-                                       (lds_void*)(st + TILEA + (wave * LPWB + j) * 1024), 16,
-                                       0, 0);
-  };
-
-  f32x4 acc[4][NJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // fragments of k-step ks of a stage: A rows wm.., B rows wn.. of the tile
-  auto load_frags = [&](const unsigned char* st, int ks, bf16x8* af, bf16x8* bfr) {
-    const int kc = ks * 4 + (lane >> 4);  // 16-byte chunk of the k-slice
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm + i * 16 + (lane & 15);
-      af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = wn + j * 16 + (lane & 15);
-      bfr[j] = *(const bf16x8*)(st + TILEA + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
-    }
-  };
-
-  const int nk = Kd / BK;
-  for (int kt = 0; kt < S - 1 && kt < nk; ++kt) issue(kt);
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt landed for this wave; after the barrier it has for every wave,
-    // and every wave has finished reading tile kt-1, whose stage is refilled
-    wait_vm_tiles<LPWA + LPWB, S - 2>(min(S - 2, nk - 1 - kt));
-    block_sync_lds();
-    if (kt + S - 1 < nk) issue(kt + S - 1);
-    const unsigned char* st = gsm + (kt % S) * STAGE;
-    bf16x8 af[2][4], bfr[2][NJ];
-    load_frags(st, 0, af[0], bfr[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      if (ks + 1 < BK / 32) load_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = tile_n + wn + j * 16 + (lane & 15);
-      if (col >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = tile_m + wm + i * 16 + (lane >> 4) * 4 + r;
-        if (row >= M) continue;
-        float* c = row < m_split ? C0 + (size_t)row * ldc + col
-                                 : C1 + (size_t)(row - m_split) * ldc + col;
-        *c = accumulate ? *c + acc[i][j][r] : acc[i][j][r];
-      }
-    }
-}
-
-// Measured on 4096 x 2048 x 2608 (all with the XCD-aware order, which alone
-// takes the 128 x 128 tile from 64 to 60 us): 128 x 192 tiles, BK = 64 and
-// 2 stages (80 KB of LDS, two workgroups per CU; 448 tiles fill the 512
-// workgroup slots in one round) 54 us; 128 x 160 67 us; 128 x 192 with BK = 32
-// and 2 or 3 stages 57-61 us; 128 x 128 with BK = 32 and 4 stages 71 us.
-constexpr int GEMM_BK = 64, GEMM_STAGES = 2, GEMM_NJ = 6;
 
 // ------------------------------------------------------------------ fp32 GEMM
 // fp32 inputs: plain LDS-tiled VALU GEMM, 64 x 64 tile, 4 x 4 outputs/thread.
@@ -763,25 +577,10 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
 
 }  // namespace
 
-hipError_t launch_gemm_bt_bf16(const void* A, const void* B0, const void* B1, int n_split, int M,
-                               int N, int Kd, float* C0, float* C1, int m_split, int ldc,
-                               bool accumulate, hipStream_t s) {
-  constexpr int S = GEMM_STAGES, BK = GEMM_BK, NJ = GEMM_NJ;
-  if (Kd % BK != 0 || M <= 0 || N <= 0) return hipErrorInvalidValue;
-  const int tiles_n = (N + 32 * NJ - 1) / (32 * NJ);
-  const int tiles = ((M + 127) / 128) * tiles_n;
-  const int per_xcd = (tiles + 7) / 8;
-  const size_t lds = (size_t)S * (128 + 32 * NJ) * 2 * BK;
-  hipLaunchKernelGGL((gemm_bt_bf16_pipe<BK, S, NJ>), dim3(8 * per_xcd), dim3(256), lds, s,
-                     (const uint16_t*)A, (const uint16_t*)B0, (const uint16_t*)B1, M, N, Kd,
-                     n_split, tiles_n, per_xcd, C0, C1, m_split, ldc, accumulate ? 1 : 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int L, int d,
                               int Nr, int Nc, omni_dtype dt, float* logits, hipStream_t s) {
   const int Ntot = Nr + Nc;
-  if (dt == OMNI_BF16 && d % GEMM_BK == 0) {
+  if (dt == OMNI_BF16 && d % GEMM_KTILE == 0) {
     return launch_gemm_bt_bf16(x, Wr, Wc, Nr, L, Ntot, d, logits, logits, L, Ntot, false, s);
   } else if (dt == OMNI_BF16) {  // d not a multiple of BK: zero-filled partial k-tile
     dim3 grid((Ntot + GBN - 1) / GBN, (L + GBM - 1) / GBM);

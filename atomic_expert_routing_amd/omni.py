@@ -16,15 +16,16 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 2
+_ABI_VERSION = 3
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
-OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD = 3, 4
+OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
 EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
-            "omni_workspace_bytes", "omni_status_string", "omni_last_error", "omni_abi_version")
+            "omni_shared_mlp", "omni_workspace_bytes", "omni_status_string", "omni_last_error",
+            "omni_abi_version")
 
 
 class OmniError(RuntimeError):
@@ -59,11 +60,13 @@ def library() -> ctypes.CDLL:
                                          vp, sz, vp]
     lib.omni_router_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, sz, vp]
+    lib.omni_shared_mlp.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp,
+                                    ctypes.c_int, vp, sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
     for f in ("omni_router", "omni_schedule", "omni_expert_forward",
               "omni_expert_forward_token_centric", "omni_expert_backward",
-              "omni_router_backward", "omni_workspace_bytes"):
+              "omni_router_backward", "omni_shared_mlp", "omni_workspace_bytes"):
         getattr(lib, f).restype = ctypes.c_int
     lib.omni_status_string.argtypes = [ctypes.c_int]
     lib.omni_status_string.restype = ctypes.c_char_p
@@ -264,6 +267,21 @@ def omni_router_backward(x, Wr, Wc, idx, gate, dgate, dx, dWr=None, dWc=None, ws
     pw, nw = _workspace(ws, need, x.device)
     _check(library().omni_router_backward(*args, pw, nw, _stream(stream)), "omni_router_backward")
     return dx, dWr, dWc
+
+
+def omni_shared_mlp(x, Wg, Wu, Wd, y=None, accumulate=False, ws=None, stream=None):
+    """Shared dense MLP: y = MLP(x), or y += MLP(x) with accumulate -> y [L, d] f32."""
+    L, d = x.shape
+    F = Wg.shape[0]
+    dt = _dtype_code(x)
+    y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
+    args = (_dev(x, "x"), _dev(Wg, "Wg", x.dtype, (F, d)), _dev(Wu, "Wu", x.dtype, (F, d)),
+            _dev(Wd, "Wd", x.dtype, (d, F)), L, d, F, dt, _dev(y, "y", torch.float32, (L, d)),
+            1 if accumulate else 0)
+    need = omni_workspace_bytes(OMNI_OP_SHARED_MLP, L, d, 1, 1, 1, F, 1, dt) if ws is None else 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_shared_mlp(*args, pw, nw, _stream(stream)), "omni_shared_mlp")
+    return y
 
 
 class RoutedBranch:

@@ -32,7 +32,7 @@ import numpy as np
 import torch
 
 ROWS_PER_BLOCK = 65536
-_TID = {"x": 0, "Wr": 1, "Wc": 2, "W": 3, "V": 4, "centres": 5, "cluster": 6, "dy": 7}
+_TID = {"x": 0, "Wr": 1, "Wc": 2, "W": 3, "V": 4, "centres": 5, "cluster": 6, "dy": 7, "Wg": 8, "Wu": 9, "Wd": 10}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -139,6 +139,22 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
         Wc=normal_rows("Wc", w.Nc, w.d, std, seed, device, dt),
         W=normal_rows("W", w.N, w.d, std, seed, device, dt),
         V=normal_rows("V", w.N, w.d, std, seed, device, dt),
+    )
+
+
+def mlp_hidden(d: int) -> int:
+    """Hidden width of the shared SwiGLU MLP: 8d/3 rounded up to 128."""
+    return -(-8 * d // (3 * 128)) * 128
+
+
+def mlp_weights(L_unused, d: int, F: int, dtype: str = "bf16", seed: int = 0,
+                device="cpu") -> dict:
+    """Wg, Wu [F, d] ~ N(0, 1/d) and Wd [d, F] ~ N(0, 1/F), in the given dtype."""
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    return dict(
+        Wg=normal_rows("Wg", F, d, 1.0 / math.sqrt(d), seed, device, dt),
+        Wu=normal_rows("Wu", F, d, 1.0 / math.sqrt(d), seed, device, dt),
+        Wd=normal_rows("Wd", d, F, 1.0 / math.sqrt(F), seed, device, dt),
     )
 
 

@@ -139,6 +139,39 @@ def cpu_baseline(inp, w, n_tok, seed):
     }
 
 
+def time_mlp(inp, w, steps, seed, step_ms):
+    """The layer's shared dense MLP (SwiGLU, d_ff = 8d/3 rounded to 128),
+    accumulated into a routed output; the layer is the routed step plus it."""
+    import torch
+
+    from atomic_expert_routing_amd import omni, synth
+
+    F = synth.mlp_hidden(w.d)
+    mw = synth.mlp_weights(w.L, w.d, F, w.dtype, seed=seed, device="cuda")
+    y = torch.zeros((w.L, w.d), dtype=torch.float32, device="cuda")
+    dt = omni.OMNI_BF16 if w.dtype == "bf16" else omni.OMNI_F32
+    ws = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, w.L, w.d, 1, 1, 1, F, 1, dt),
+                     dtype=torch.uint8, device="cuda")
+    run = lambda: omni.omni_shared_mlp(inp["x"], mw["Wg"], mw["Wu"], mw["Wd"], y, True, ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = statistics.median(ts)
+    flops = 3 * 2.0 * w.L * w.d * F
+    return {"d_ff": F, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "layer_ms": round(step_ms + ms, 4),
+            "note": "SwiGLU MLP; layer = routed branch step (events) + this MLP"}
+
+
 def time_backward(inp, w, br, steps, seed):
     """omni_expert_backward + omni_router_backward on the step's routing, for a
     seeded upstream gradient; preallocated outputs and workspaces.  The expert
@@ -357,6 +390,8 @@ def main():
     tc_ms = statistics.median(tc_times)
     out["token_centric_assembly_ms"] = round(tc_ms, 4)
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
+
+    out["shared_mlp"] = time_mlp(inp, w, args.steps, args.seed, step_ev_ms)
 
     if not args.no_backward:
         out["backward"] = time_backward(inp, w, br, args.steps, args.seed)

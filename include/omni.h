@@ -11,6 +11,8 @@
  * The backward of the branch runs in two more calls:
  *   omni_expert_backward  dx (expert part), d gate, dW and dV of used experts
  *   omni_router_backward  dW_r, dW_c, and the router part added into dx
+ * and the layer's other branch in one:
+ *   omni_shared_mlp       the shared dense MLP, added into (or written to) y
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller, row-major and
@@ -41,7 +43,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 2
+#define OMNI_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -64,7 +66,8 @@ typedef enum {
   OMNI_OP_SCHEDULE = 1,
   OMNI_OP_EXPERT_FORWARD = 2,
   OMNI_OP_EXPERT_BACKWARD = 3,
-  OMNI_OP_ROUTER_BACKWARD = 4
+  OMNI_OP_ROUTER_BACKWARD = 4,
+  OMNI_OP_SHARED_MLP = 5 /* omni_workspace_bytes takes d_ff in its N argument */
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -234,6 +237,31 @@ OMNI_API omni_status omni_router_backward(const void* x, const void* Wr, const v
                                           int64_t Nc, int64_t K, omni_dtype dt, float* dx,
                                           float* dWr, float* dWc, void* ws, size_t ws_bytes,
                                           void* stream);
+
+/*
+ * omni_shared_mlp - the shared dense MLP branch of the layer.
+ * Source: OmniMoE digest, method paragraph, step 1 (y = (g . sigma(x w^T)) v
+ * + MLP(x)); gist.science resume section 2.1 (a standard dense MLP branch,
+ * active for every input).  The pages give no shape; it is read as a SwiGLU
+ * block (the digest's SwiGLU remark has no gate vector to act on in an
+ * atomic expert):
+ *   MLP(x) = (SiLU(x Wg^T) * (x Wu^T)) Wd^T
+ *
+ *   x       [L, d]      dtype dt
+ *   Wg, Wu  [d_ff, d]   dtype dt   gate and up projections
+ *   Wd      [d, d_ff]   dtype dt   down projection
+ *   y       [L, d] fp32 out: y = MLP(x) when accumulate == 0, y += MLP(x)
+ *                       otherwise (after omni_expert_forward this gives the
+ *                       whole layer, routed branch + MLP)
+ * bf16: products on MFMA with fp32 accumulation; the intermediate
+ * SiLU(g) * u is rounded to bf16 before the down projection.  fp32: fp32
+ * throughout.  Requires d_ff >= 1; bf16 also needs d % 64 == 0 and
+ * d_ff % 64 == 0.  Workspace: the intermediate [L, d_ff]
+ * (omni_workspace_bytes(OMNI_OP_SHARED_MLP, ..., N = d_ff, ...)).
+ */
+OMNI_API omni_status omni_shared_mlp(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                                     int64_t L, int64_t d, int64_t d_ff, omni_dtype dt, float* y,
+                                     int accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * omni_workspace_bytes - workspace size needed by one call of `op` with

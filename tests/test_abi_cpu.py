@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 2
+    assert lib.omni_abi_version() == 3
 
 
 def test_status_strings():
@@ -154,6 +154,21 @@ def test_backward_workspace_sizes_and_validation():
     s = lib.omni_router_backward(fake, fake, fake, fake, fake, fake, 4, 8, 2, 2, 2, omni.OMNI_BF16,
                                  fake, fake, fake, fake, 16, None)
     assert s == omni.OMNI_ERR_WORKSPACE
+
+
+def test_shared_mlp_workspace_and_validation():
+    # bf16: the bf16 intermediate [L, d_ff]; fp32: two fp32 [L, d_ff] buffers
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, L=4096, d=2048, N=5504) == 4096 * 5504 * 2
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, L=64, d=64, N=128,
+                                     dtype=omni.OMNI_F32) == 2 * 64 * 128 * 4
+    for kw, st in ((dict(d=72, N=128), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(d=64, N=100), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(d=64, N=0), omni.OMNI_ERR_INVALID_ARG)):
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, L=8, **kw)
+        assert e.value.status == st
+    # fp32 takes any d % 8 == 0 and any d_ff
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, L=8, d=72, N=100, dtype=omni.OMNI_F32) > 0
 
 
 def test_binding_rejects_cpu_tensors():

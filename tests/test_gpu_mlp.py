@@ -1,0 +1,100 @@
+"""GPU parity of the shared dense MLP (omni_shared_mlp) against the oracle.
+
+fp32 inputs run in fp32 throughout and are held to the fp32-arithmetic bound.
+bf16 inputs round the intermediate a = SiLU(x Wg^T) * (x Wu^T) to bf16 before
+the down projection (as bf16 MLPs do); each element then carries a relative
+error of at most 2^-9, so every output element must lie within
+2^-9 * (|a| |Wd|^T) of the float64 result, plus fp32 accumulation slack.
+That elementwise bound is computed from the oracle's own a.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from atomic_expert_routing_amd import omni, synth
+from oracle import omni_oracle as O
+from parity import RTOL_FP32_ARITH, check_y, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    omni.library()
+
+
+def check_mlp(x, Wg, Wu, Wd, got, base=None):
+    """got = base + MLP(x) on the rows given; returns the worst bound ratio."""
+    x, Wg, Wu, Wd = (to_np(t).astype(np.float64) for t in (x, Wg, Wu, Wd))
+    a = O.silu(x @ Wg.T) * (x @ Wu.T)
+    want = a @ Wd.T
+    got = to_np(got).astype(np.float64)
+    if base is not None:
+        got = got - to_np(base).astype(np.float64)
+    err = np.abs(got - want)
+    bound = (2.0 ** -9 + 2.0 ** -20) * (np.abs(a) @ np.abs(Wd).T) + 1e-6 * np.abs(want).max()
+    ratio = float((err / bound).max())
+    assert ratio <= 1.0, f"error exceeds the bf16-intermediate bound by {ratio:.3g}x"
+    return ratio, float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+CASES = [(64, 64, 128, "bf16"), (130, 64, 192, "bf16"), (200, 256, 704, "bf16"),
+         (300, 2048, 5504, "bf16"), (64, 64, 128, "f32"), (33, 72, 100, "f32")]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "L{}_d{}_F{}_{}".format(*c))
+def test_shared_mlp_matches_oracle(case):
+    L, d, F, dtype = case
+    say(f"mlp case {case}")
+    w, inp = synth.make_case(L, d, 4, 4, 2, 4, dtype, seed=2)
+    mw = synth.mlp_weights(L, d, F, dtype, seed=2)
+    x = inp["x"].cuda()
+    Wg, Wu, Wd = (mw[k].cuda() for k in ("Wg", "Wu", "Wd"))
+    y = omni.omni_shared_mlp(x, Wg, Wu, Wd)
+    torch.cuda.synchronize()
+    if dtype == "f32":
+        want = O.shared_mlp(inp["x"], mw["Wg"], mw["Wu"], mw["Wd"])
+        nrm, _ = check_y(y, want, RTOL_FP32_ARITH)
+        say(f"  fp32 norm err {nrm:.1e}")
+    else:
+        ratio, nrm = check_mlp(x, Wg, Wu, Wd, y)
+        say(f"  worst error / bound {ratio:.2f}, norm err {nrm:.1e}")
+
+
+def test_accumulate_adds_to_the_routed_output():
+    """omni_shared_mlp(accumulate) after omni_expert_forward gives the layer."""
+    w, inp_cpu = synth.make_case(130, 128, 12, 10, 8, 8, "bf16", seed=4)
+    F = synth.mlp_hidden(128)
+    mw = {k: v.cuda() for k, v in synth.mlp_weights(130, 128, F, "bf16", seed=4).items()}
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, torch.bfloat16)
+    br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    routed = br.y.clone()
+    omni.omni_shared_mlp(inp["x"], mw["Wg"], mw["Wu"], mw["Wd"], y=br.y, accumulate=True)
+    alone = omni.omni_shared_mlp(inp["x"], mw["Wg"], mw["Wu"], mw["Wd"])
+    torch.cuda.synchronize()
+    # the accumulated result is routed + the stand-alone MLP, element by element
+    assert torch.equal(br.y, routed + alone)
+    check_mlp(inp["x"], mw["Wg"], mw["Wu"], mw["Wd"], br.y, base=routed)
+
+
+def test_full_size_mlp_sampled():
+    """4096 tokens, d = 2048, d_ff = 5504: sampled rows against the oracle."""
+    w = synth.WORKLOADS[synth.HEADLINE]
+    F = synth.mlp_hidden(w.d)
+    x = synth.make_inputs(w, seed=0, device="cuda")["x"]
+    mw = synth.mlp_weights(w.L, w.d, F, "bf16", seed=0, device="cuda")
+    y = omni.omni_shared_mlp(x, mw["Wg"], mw["Wu"], mw["Wd"])
+    torch.cuda.synchronize()
+    rs = np.random.Generator(np.random.PCG64(5))
+    toks = np.unique(np.concatenate([[0, w.L - 1], rs.choice(w.L, 30, replace=False)]))
+    tk = torch.as_tensor(toks, device="cuda")
+    ratio, nrm = check_mlp(x[tk], mw["Wg"], mw["Wu"], mw["Wd"], y[tk])
+    say(f"  full size: worst error / bound {ratio:.2f}, norm err {nrm:.1e}")
