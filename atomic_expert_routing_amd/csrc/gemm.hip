@@ -14,11 +14,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int GEMM_PLAIN = 0, GEMM_SWIGLU = 1;
 
 // ------------------------------------------------------------------ bf16 GEMM, pipelined
-// The same 128 x 128 tile and wave layout, with the k-tiles (BK deep)
+// Output tiles per workgroup (below), with the k-tiles (BK deep)
 // streamed through S LDS stages by direct global->LDS loads
 // (global_load_lds_dwordx4: each instruction writes 64 lanes x 16 bytes of
 // LDS without register staging), so S-1 k-tiles are in flight while one is
-// multiplied.  A stage holds the A and B tiles as 128 rows x 2*BK bytes; the
+// multiplied.  A stage holds the A and B tiles as rows of 2*BK bytes; the
 // 16-byte chunk c of row r sits in slot c ^ swz(r), which spreads the 16
 // rows read by one ds_read_b128 over 16 distinct bank groups.  Rows past L
 // or N_r+N_c are loaded from a clamped row (their results are never
@@ -68,8 +68,9 @@ __device__ __forceinline__ int chunk_swz(int r) {
 // (gate projection) and B1 (up projection), N = 2 d_ff, and the epilogue
 // writes bf16 SiLU(gate) * up to Cb [M, ldc = d_ff].
 //
-// Tiles are 128 x (32 NJ): 4 waves as 2 x 2, each 64 x 16 NJ outputs held as
-// 4 x NJ MFMA 16x16 accumulators.  The grid is one-dimensional and the tile
+// Tiles are (16 MI WVM) x (16 NJ WVN): WVM x WVN waves, each 16 MI x 16 NJ
+// outputs held as MI x NJ MFMA 16x16 accumulators (the default: 128 x 192,
+// 2 x 2 waves of 64 x 96).  The grid is one-dimensional and the tile
 // order is XCD-aware: workgroup b runs on XCD b % 8 and takes tile
 // (b % 8) * per_xcd + b / 8 of the row-major tile order, so that each XCD
 // sweeps a contiguous band of output rows and the x and W panels its
@@ -80,8 +81,8 @@ __device__ __forceinline__ int chunk_swz(int r) {
 // come from B0, the others from B1 (the router stacks W_r over W_c); C rows
 // m < m_split go to C0, the others to C1 (row stride ldc), so that one product
 // can fill two separately owned matrices.
-template <int BK, int S, int NJ, int MODE>
-__global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restrict__ A,
+template <int BK, int S, int NJ, int MI, int WVM, int WVN, int MODE>
+__global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ B0,
                                                          const uint16_t* __restrict__ B1,
                                                          int M, int N, int Kd, int n_split,
@@ -91,24 +92,28 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
                                                          int ldc, int accumulate,
                                                          uint16_t* __restrict__ Cb) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
-  constexpr int TN = 32 * NJ;             // tile columns
+  constexpr int NW = WVM * WVN;           // waves per workgroup
+  constexpr int TM = WVM * MI * 16;       // tile rows
+  constexpr int TN = WVN * NJ * 16;       // tile columns
   constexpr int ROWB = 2 * BK;            // bytes per tile row
-  constexpr int TILEA = 128 * ROWB;       // bytes of the A tile
+  constexpr int TILEA = TM * ROWB;        // bytes of the A tile
   constexpr int TILEB = TN * ROWB;        // bytes of the B tile
   constexpr int STAGE = TILEA + TILEB;
   constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;           // rows per 1 KB load instruction
-  constexpr int LPWA = TILEA / 1024 / 4;  // loads per wave per k-tile, A
-  constexpr int LPWB = TILEB / 1024 / 4;  // and B
-  static_assert(TILEB % 4096 == 0, "B tile must split into 1 KB loads over 4 waves");
+  constexpr int LPWA = TILEA / 1024 / NW; // loads per wave per k-tile, A
+  constexpr int LPWB = TILEB / 1024 / NW; // and B
+  static_assert(TILEA % (1024 * NW) == 0 && TILEB % (1024 * NW) == 0,
+                "tiles must split into 1 KB loads over the waves");
+  static_assert(MODE != GEMM_SWIGLU || NJ % 2 == 0, "SwiGLU pairs MFMA column tiles");
   static_assert(S >= 2 && S <= 5, "pipeline depth");
   const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int tiles_m = (M + 127) / 128;
+  const int tiles_m = (M + TM - 1) / TM;
   if (t >= tiles_m * tiles_n) return;  // whole workgroup, before any barrier
-  const int tile_m = (t / tiles_n) * 128, tile_n = (t % tiles_n) * TN;
+  const int tile_m = (t / tiles_n) * TM, tile_n = (t % tiles_n) * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (16 * NJ);
+  const int wm = (wave / WVN) * (16 * MI), wn = (wave % WVN) * (16 * NJ);
 
   // load j of wave w fills bytes [(LPW*w + j) * 1024, +1024) of a tile
   const uint16_t* asrc[LPWA];
@@ -146,9 +151,9 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
                                        0, 0);
   };
 
-  f32x4 acc[4][NJ];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
   auto load_frags = [&](const unsigned char* st, int ks, bf16x8* af, bf16x8* bfr) {
     const int kc = ks * 4 + (lane >> 4);  // 16-byte chunk of the k-slice
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       const int r = wm + i * 16 + (lane & 15);
       af[i] = *(const bf16x8*)(st + r * ROWB + ((kc ^ chunk_swz<BK>(r)) << 4));
     }
@@ -176,13 +181,13 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
     block_sync_lds();
     if (kt + S - 1 < nk) issue(kt + S - 1);
     const unsigned char* st = gsm + (kt % S) * STAGE;
-    bf16x8 af[2][4], bfr[2][NJ];
+    bf16x8 af[2][MI], bfr[2][NJ];
     load_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       if (ks + 1 < BK / 32) load_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][j],
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
     // MFMA tiles 2q and 2q+1 of a wave hold the gate and up projections of
     // the same 16 hidden units: out = SiLU(g) * u, rounded to bf16
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int q = 0; q < NJ / 2; ++q) {
         const int col = (((tile_n + wn) >> 5) + q) * 16 + (lane & 15);
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = tile_n + wn + j * 16 + (lane & 15);
@@ -227,12 +232,28 @@ __global__ __launch_bounds__(256) void gemm_bt_bf16_pipe(const uint16_t* __restr
     }
 }
 
-// Measured on 4096 x 2048 x 2608 (all with the XCD-aware order, which alone
-// takes the 128 x 128 tile from 64 to 60 us): 128 x 192 tiles, BK = 64 and
-// 2 stages (80 KB of LDS, two workgroups per CU; 448 tiles fill the 512
-// workgroup slots in one round) 54 us; 128 x 160 67 us; 128 x 192 with BK = 32
-// and 2 or 3 stages 57-61 us; 128 x 128 with BK = 32 and 4 stages 71 us.
-constexpr int GEMM_BK = GEMM_KTILE, GEMM_STAGES = 2, GEMM_NJ = 6;
+// Two tile shapes, chosen per product by its tile count (measured on the
+// products this library runs; TFLOP/s on 2.5 PFLOP/s peak):
+//   big:   256 x 192, 8 waves (4 x 2) of 64 x 96, BK = 64, 2 stages, 112 KB
+//          of LDS (one workgroup per CU).  Best when the product has at
+//          least ~200 such tiles: 4096 x 2608 x 2048 56 us (776 TFLOP/s),
+//          4096 x 11008 x 2048 201 us (919).
+//   small: 128 x 128, 4 waves of 64 x 64, BK = 64, 2 stages, 64 KB (two or
+//          three workgroups per CU).  Best below that: 4096 x 2048 x 5504
+//          95 us (976), 2608 x 2048 x 4096 61 us (713).
+// Also measured and dropped: 128 x 192 (4 waves; 59 / 257 / 117 / 67 us on
+// the four products), 256 x 192 with 4 waves of 128 x 96 (BK 32 or 64, 2 or 3
+// stages: one wave per SIMD, 73-284 us), 256 x 256 with 8 waves and BK = 32,
+// 128 x 256.  Before the XCD-aware order the 128 x 128 tile took 64 us on the
+// router product (60 us after).
+struct GemmCfgBig {
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 6, MI = 4, WVM = 4, WVN = 2;
+};
+struct GemmCfgSmall {
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 4, MI = 4, WVM = 2, WVN = 2;
+};
+using GemmCfg = GemmCfgBig;
+constexpr int GEMM_BIG_MIN_TILES = 200;
 
 // ------------------------------------------------------------------ fp32 product
 // C[m, n] (+)= sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk], 64 x 64 tiles.
@@ -285,20 +306,33 @@ __global__ __launch_bounds__(256) void gemm_f32_strided(const float* __restrict_
   }
 }
 
-template <int MODE>
+template <int MODE, class C = GemmCfg>
 hipError_t launch_t(const void* A, const void* B0, const void* B1, int n_split, int M, int N,
                     int Kd, float* C0, float* C1, int m_split, int ldc, bool accumulate,
                     uint16_t* Cb, hipStream_t s) {
-  constexpr int S = GEMM_STAGES, BK = GEMM_BK, NJ = GEMM_NJ;
-  if (Kd % BK != 0 || M <= 0 || N <= 0) return hipErrorInvalidValue;
-  const int tiles_n = (N + 32 * NJ - 1) / (32 * NJ);
-  const int tiles = ((M + 127) / 128) * tiles_n;
+  constexpr int TM = C::WVM * C::MI * 16, TN = C::WVN * C::NJ * 16;
+  if (Kd % C::BK != 0 || M <= 0 || N <= 0) return hipErrorInvalidValue;
+  const int tiles_n = (N + TN - 1) / TN;
+  const int tiles = ((M + TM - 1) / TM) * tiles_n;
   const int per_xcd = (tiles + 7) / 8;
-  const size_t lds = (size_t)S * (128 + 32 * NJ) * 2 * BK;
-  hipLaunchKernelGGL((gemm_bt_bf16_pipe<BK, S, NJ, MODE>), dim3(8 * per_xcd), dim3(256), lds, s,
-                     (const uint16_t*)A, (const uint16_t*)B0, (const uint16_t*)B1, M, N, Kd,
-                     n_split, tiles_n, per_xcd, C0, C1, m_split, ldc, accumulate ? 1 : 0, Cb);
+  const size_t lds = (size_t)C::S * (TM + TN) * 2 * C::BK;
+  hipLaunchKernelGGL((gemm_bt_bf16_pipe<C::BK, C::S, C::NJ, C::MI, C::WVM, C::WVN, MODE>),
+                     dim3(8 * per_xcd), dim3(64 * C::WVM * C::WVN), lds, s, (const uint16_t*)A,
+                     (const uint16_t*)B0, (const uint16_t*)B1, M, N, Kd, n_split, tiles_n,
+                     per_xcd, C0, C1, m_split, ldc, accumulate ? 1 : 0, Cb);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_sel(const void* A, const void* B0, const void* B1, int n_split, int M, int N,
+                      int Kd, float* C0, float* C1, int m_split, int ldc, bool accumulate,
+                      uint16_t* Cb, hipStream_t s) {
+  const int big_tiles = ((M + 255) / 256) * ((N + 191) / 192);
+  if (big_tiles >= GEMM_BIG_MIN_TILES)
+    return launch_t<MODE, GemmCfgBig>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc,
+                                      accumulate, Cb, s);
+  return launch_t<MODE, GemmCfgSmall>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc,
+                                      accumulate, Cb, s);
 }
 
 }  // namespace
@@ -306,14 +340,15 @@ hipError_t launch_t(const void* A, const void* B0, const void* B1, int n_split, 
 hipError_t launch_gemm_bt_bf16(const void* A, const void* B0, const void* B1, int n_split, int M,
                                int N, int Kd, float* C0, float* C1, int m_split, int ldc,
                                bool accumulate, hipStream_t s) {
-  return launch_t<GEMM_PLAIN>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc, accumulate,
-                              nullptr, s);
+  return launch_sel<GEMM_PLAIN>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc, accumulate,
+                                nullptr, s);
 }
 
 hipError_t launch_gemm_swiglu_bf16(const void* A, const void* Wg, const void* Wu, int M, int F,
                                    int Kd, uint16_t* out, hipStream_t s) {
   if (F % 16 != 0) return hipErrorInvalidValue;
-  return launch_t<GEMM_SWIGLU>(A, Wg, Wu, 0, M, 2 * F, Kd, nullptr, nullptr, 0, F, false, out, s);
+  return launch_sel<GEMM_SWIGLU>(A, Wg, Wu, 0, M, 2 * F, Kd, nullptr, nullptr, 0, F, false, out,
+                                 s);
 }
 
 hipError_t gemm_f32(const float* A, long sam, long sak, const float* B, long sbn, long sbk, int M,
