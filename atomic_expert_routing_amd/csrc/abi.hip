@@ -118,6 +118,24 @@ omni_status mlp_ws(int64_t L, int64_t d, int64_t F, omni_dtype dt, size_t* out) 
   return OMNI_OK;
 }
 
+omni_status dense_router_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = check_dtype_d(dt, d)) != OMNI_OK) return s;
+  if ((s = check_tasks(L, K)) != OMNI_OK) return s;
+  if (N <= 0) return fail(OMNI_ERR_INVALID_ARG, "N must be positive (got %lld)", (long long)N);
+  if (N > I32_LIMIT) return fail(OMNI_ERR_UNSUPPORTED, "N = %lld exceeds 2^31-1", (long long)N);
+  if (K > N) return fail(OMNI_ERR_INVALID_ARG, "K = %lld exceeds N = %lld", (long long)K, (long long)N);
+  if (K > OMNI_MAX_K) return fail(OMNI_ERR_UNSUPPORTED, "K = %lld exceeds %d", (long long)K, OMNI_MAX_K);
+  if (dt == OMNI_BF16 && d % omni::GEMM_KTILE)
+    return fail(OMNI_ERR_UNSUPPORTED, "bf16 dense router needs d %% %d == 0 (d=%lld)", omni::GEMM_KTILE,
+                (long long)d);
+  const omni::DenseRouterPlan p = omni::plan_dense_router(L, N, K);
+  if ((int64_t)p.nchunks * K > I32_LIMIT / L)
+    return fail(OMNI_ERR_UNSUPPORTED, "L * candidates exceeds 2^31-1");
+  *out = p.ws_bytes;
+  return OMNI_OK;
+}
+
 omni_status check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
     return fail(OMNI_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
@@ -263,6 +281,23 @@ omni_status omni_shared_mlp(const void* x, const void* Wg, const void* Wu, const
   return hip_status(e, "shared MLP launch");
 }
 
+omni_status omni_dense_router(const void* x, const void* Wn, int64_t L, int64_t d, int64_t N,
+                              int64_t K, omni_dtype dt, int32_t* idx, float* score, float* gate,
+                              void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = dense_router_ws(L, d, N, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !Wn || !idx || !score || !gate)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_dense_router: NULL array pointer");
+  if (!aligned16(x) || !aligned16(Wn))
+    return fail(OMNI_ERR_INVALID_ARG, "omni_dense_router: x and Wn must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::DenseRouterPlan plan = omni::plan_dense_router(L, N, K);
+  hipError_t e = omni::launch_dense_router(x, Wn, (int)L, (int)d, (int)N, (int)K, dt, idx, score,
+                                           gate, plan, ws, (hipStream_t)stream);
+  return hip_status(e, "dense router launch");
+}
+
 omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
                                  int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
   if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");
@@ -275,6 +310,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_EXPERT_BACKWARD: s = expert_bwd_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_ROUTER_BACKWARD: s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need); break;
     case OMNI_OP_SHARED_MLP: s = mlp_ws(L, d, N, dt, &need); break;
+    case OMNI_OP_DENSE_ROUTER: s = dense_router_ws(L, d, N, K, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

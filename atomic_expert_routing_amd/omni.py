@@ -16,16 +16,17 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 3
+_ABI_VERSION = 4
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
+OMNI_OP_DENSE_ROUTER = 6
 EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
-            "omni_shared_mlp", "omni_workspace_bytes", "omni_status_string", "omni_last_error",
-            "omni_abi_version")
+            "omni_shared_mlp", "omni_dense_router", "omni_workspace_bytes", "omni_status_string",
+            "omni_last_error", "omni_abi_version")
 
 
 class OmniError(RuntimeError):
@@ -62,11 +63,14 @@ def library() -> ctypes.CDLL:
                                          ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.omni_shared_mlp.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp,
                                     ctypes.c_int, vp, sz, vp]
+    lib.omni_dense_router.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
+                                      sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
     for f in ("omni_router", "omni_schedule", "omni_expert_forward",
               "omni_expert_forward_token_centric", "omni_expert_backward",
-              "omni_router_backward", "omni_shared_mlp", "omni_workspace_bytes"):
+              "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
+              "omni_workspace_bytes"):
         getattr(lib, f).restype = ctypes.c_int
     lib.omni_status_string.argtypes = [ctypes.c_int]
     lib.omni_status_string.restype = ctypes.c_char_p
@@ -282,6 +286,24 @@ def omni_shared_mlp(x, Wg, Wu, Wd, y=None, accumulate=False, ws=None, stream=Non
     pw, nw = _workspace(ws, need, x.device)
     _check(library().omni_shared_mlp(*args, pw, nw, _stream(stream)), "omni_shared_mlp")
     return y
+
+
+def omni_dense_router(x, Wn, K: int, idx=None, score=None, gate=None, ws=None, stream=None):
+    """Fully connected router over all N experts -> (idx, score, gate), each [L, K]."""
+    L, d = x.shape
+    N = Wn.shape[0]
+    dt = _dtype_code(x)
+    kw = dict(device=x.device)
+    idx = torch.empty((L, K), dtype=torch.int32, **kw) if idx is None else idx
+    score = torch.empty((L, K), dtype=torch.float32, **kw) if score is None else score
+    gate = torch.empty((L, K), dtype=torch.float32, **kw) if gate is None else gate
+    args = (_dev(x, "x"), _dev(Wn, "Wn", x.dtype, (N, d)), L, d, N, K, dt,
+            _dev(idx, "idx", torch.int32, (L, K)), _dev(score, "score", torch.float32, (L, K)),
+            _dev(gate, "gate", torch.float32, (L, K)))
+    need = omni_workspace_bytes(OMNI_OP_DENSE_ROUTER, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_dense_router(*args, pw, nw, _stream(stream)), "omni_dense_router")
+    return idx, score, gate
 
 
 class RoutedBranch:

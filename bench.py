@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import statistics
 import sys
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MB "
                          "Infinity Cache, timed with events (0 to skip)")
+    ap.add_argument("--no-dense-router", action="store_true",
+                    help="skip timing the fully connected router of the ablation")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward calls")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -170,6 +173,42 @@ def time_mlp(inp, w, steps, seed, step_ms):
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "layer_ms": round(step_ms + ms, 4),
             "note": "SwiGLU MLP; layer = routed branch step (events) + this MLP"}
+
+
+def time_dense_router(inp, w, router_ms, seed, reps=3):
+    """The ablation's fully connected router over all N experts (seeded
+    Wn [N, d] ~ N(0, 1/d)), against the Cartesian router stage."""
+    import torch
+
+    from atomic_expert_routing_amd import omni, synth
+
+    Wn = synth.normal_rows("W", w.N, w.d, 1.0 / math.sqrt(w.d), seed + 1, "cuda",
+                           w.torch_dtype)
+    dt = omni.OMNI_BF16 if w.dtype == "bf16" else omni.OMNI_F32
+    ws = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, w.L, w.d, 1, 1, w.K,
+                                               w.N, 1, dt), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((w.L, w.K), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.L, w.K), dtype=torch.float32, device="cuda")
+    g = torch.empty((w.L, w.K), dtype=torch.float32, device="cuda")
+    run = lambda: omni.omni_dense_router(inp["x"], Wn, w.K, idx, sc, g, ws)
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = statistics.median(ts)
+    flops = 2.0 * w.L * w.d * w.N
+    del Wn, ws
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "logit_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "vs_cartesian_router": round(ms / router_ms, 1),
+            "note": "s = x Wn^T over all N experts in 65536-expert chunks, exact top-K, "
+                    "LogSoftmax over N; the pages report 30.6x latency for this substitution"}
 
 
 def time_backward(inp, w, br, steps, seed):
@@ -392,6 +431,8 @@ def main():
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
 
     out["shared_mlp"] = time_mlp(inp, w, args.steps, args.seed, step_ev_ms)
+    if not args.no_dense_router:
+        out["dense_router"] = time_dense_router(inp, w, router_ms, args.seed)
 
     if not args.no_backward:
         out["backward"] = time_backward(inp, w, br, args.steps, args.seed)

@@ -13,6 +13,8 @@
  *   omni_router_backward  dW_r, dW_c, and the router part added into dx
  * and the layer's other branch in one:
  *   omni_shared_mlp       the shared dense MLP, added into (or written to) y
+ * The router the pages' ablation substitutes is also provided, as a baseline:
+ *   omni_dense_router     fully connected router over all N experts
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller, row-major and
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 3
+#define OMNI_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -67,7 +69,8 @@ typedef enum {
   OMNI_OP_EXPERT_FORWARD = 2,
   OMNI_OP_EXPERT_BACKWARD = 3,
   OMNI_OP_ROUTER_BACKWARD = 4,
-  OMNI_OP_SHARED_MLP = 5 /* omni_workspace_bytes takes d_ff in its N argument */
+  OMNI_OP_SHARED_MLP = 5, /* omni_workspace_bytes takes d_ff in its N argument */
+  OMNI_OP_DENSE_ROUTER = 6
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -262,6 +265,29 @@ OMNI_API omni_status omni_router_backward(const void* x, const void* Wr, const v
 OMNI_API omni_status omni_shared_mlp(const void* x, const void* Wg, const void* Wu, const void* Wd,
                                      int64_t L, int64_t d, int64_t d_ff, omni_dtype dt, float* y,
                                      int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_dense_router - the fully connected router of the pages' ablation.
+ * Source: makerbund article, section 5 (replacing the Cartesian Product
+ * Router by a conventional fully connected router raises latency and memory
+ * sharply); the router conventions of omni_router otherwise:
+ *   s = x Wn^T over all N experts, p = LogSoftmax(s) over the N experts,
+ *   top-K under (p desc, n asc), gate = softmax over the K selected p.
+ *
+ *   x      [L, d]   dtype dt
+ *   Wn     [N, d]   dtype dt   one routing vector per expert
+ *   idx    [L, K]   int32 out  ids, rows ordered by (score desc, id asc)
+ *   score  [L, K]   fp32 out   p at the selected ids
+ *   gate   [L, K]   fp32 out   softmax over the K selected scores
+ * It costs O(N d) per token against O(sqrt(N) d) for omni_router.  The
+ * logits are formed 65536 experts at a time (a [L, 65536] fp32 buffer in the
+ * workspace), never for all N at once.  Requires 1 <= K <= min(N,
+ * OMNI_MAX_K), N < 2^31; bf16 also needs d % 64 == 0.
+ */
+OMNI_API omni_status omni_dense_router(const void* x, const void* Wn, int64_t L, int64_t d,
+                                       int64_t N, int64_t K, omni_dtype dt, int32_t* idx,
+                                       float* score, float* gate, void* ws, size_t ws_bytes,
+                                       void* stream);
 
 /*
  * omni_workspace_bytes - workspace size needed by one call of `op` with

@@ -318,20 +318,27 @@ def layer_forward(x, Wr, Wc, W, V, K, B, Wg, Wu, Wd):
 # Cartesian Product Router by a fully connected router over all N experts]
 # ---------------------------------------------------------------------------
 
+def dense_select(s, K):
+    """The dense router's steps after the logits: p = LogSoftmax(s) over the
+    N experts, top-K under (p desc, n asc), gate = softmax over the K
+    selected scores.  s [L, N].  Returns (idx [L,K] int64, score, gate)."""
+    s = as_f64(s)
+    N = s.shape[1]
+    if not 1 <= K <= N:
+        raise ValueError("K must lie in [1, N]")
+    p = log_softmax(s)
+    n_all = np.arange(N, dtype=np.int64)
+    idx = np.empty((s.shape[0], K), np.int64)
+    score = np.empty((s.shape[0], K), F64)
+    for t in range(s.shape[0]):
+        idx[t], score[t] = _take_topk(p[t], n_all, K)
+    return idx, score, gate_softmax(score)
+
+
 def dense_route(x, Wn, K):
     """Fully connected router: s = x Wn^T over all N experts (Wn [N, d]),
     p = LogSoftmax(s) over the N experts, top-K under (p desc, n asc),
     gate = softmax over the K selected scores (the same conventions as the
     Cartesian router).  Returns (idx [L,K] int64, score [L,K], gate [L,K]).
     """
-    x, Wn = as_f64(x), as_f64(Wn)
-    N = Wn.shape[0]
-    if not 1 <= K <= N:
-        raise ValueError("K must lie in [1, N]")
-    p = log_softmax(x @ Wn.T)
-    n_all = np.arange(N, dtype=np.int64)
-    idx = np.empty((x.shape[0], K), np.int64)
-    score = np.empty((x.shape[0], K), F64)
-    for t in range(x.shape[0]):
-        idx[t], score[t] = _take_topk(p[t], n_all, K)
-    return idx, score, gate_softmax(score)
+    return dense_select(as_f64(x) @ as_f64(Wn).T, K)

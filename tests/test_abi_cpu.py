@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 3
+    assert lib.omni_abi_version() == 4
 
 
 def test_status_strings():
@@ -169,6 +169,27 @@ def test_shared_mlp_workspace_and_validation():
         assert e.value.status == st
     # fp32 takes any d % 8 == 0 and any d_ff
     assert omni.omni_workspace_bytes(omni.OMNI_OP_SHARED_MLP, L=8, d=72, N=100, dtype=omni.OMNI_F32) > 0
+
+
+def test_dense_router_workspace_and_validation():
+    # chunk logits [L, 65536] fp32 + candidates (value, id) [L, chunks*K] + partials
+    L, N, K = 4096, 1700416, 128
+    chunks = -(-N // 65536)
+    ws = omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=L, d=2048, K=K, N=N)
+    assert ws == L * 65536 * 4 + 2 * L * chunks * K * 4 + L * chunks * 8
+    small = omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=8, d=64, K=4, N=100)
+    assert small >= 8 * 100 * 4
+    for kw, st in ((dict(K=101, N=100), omni.OMNI_ERR_INVALID_ARG),
+                   (dict(K=600, N=1000), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(d=72, K=4, N=100), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(N=0, K=1), omni.OMNI_ERR_INVALID_ARG)):
+        args = dict(L=8, d=64)
+        args.update(kw)
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, **args)
+        assert e.value.status == st
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=8, d=72, K=4, N=100,
+                                     dtype=omni.OMNI_F32) > 0
 
 
 def test_binding_rejects_cpu_tensors():
