@@ -5,21 +5,16 @@
 //   s = x Wn^T over all N experts (Wn [N, d]), p = LogSoftmax(s) over N,
 //   top-K under (p desc, n asc), gate = softmax over the K selected scores.
 //
-// The experts are processed in chunks of DENSE_ROUTER_CHUNK.  For each chunk an MFMA
-// (or, for fp32 inputs, VALU) product writes the chunk's logits [L, nc];
-// dense_select then picks, per token, the chunk's K largest logits (ties to
-// the smaller expert id) and the chunk's (max, sum of exp(s - max)).  Every
-// global top-K element is in its chunk's top K, so a final dense_select over
-// the L x (chunks x K) candidates gives the global top K; it also combines
-// the partial sums into the LogSoftmax constant and writes ids, scores and
-// gates sorted by (score desc, id asc).
-//
-// dense_select is an MSD radix select over 64-bit keys (the order-preserving
-// image of the value, then the complemented id): an 11-bit histogram pass
-// (with the online max / sum of exp in chunk mode), refined by further
-// digits only while the boundary bucket is larger than the LDS buffer; then
-// one pass collects everything above the boundary bucket and the bucket
-// itself, which is sorted exactly in LDS.
+// The experts are processed in chunks of DENSE_ROUTER_CHUNK.  For each chunk
+// an MFMA (or, for fp32 inputs, VALU) product writes the chunk's logits
+// [L, nc]; dense_chunk then updates, per token, a running top K (64-bit keys:
+// the order-preserving image of the logit, then the complemented id, so ties
+// go to the smaller id) and the chunk's (max, sum of exp(s - max)).  Only
+// logits above the token's current K-th key can enter, so one pass per chunk
+// usually suffices; when too many pass (the first chunk, or rising logits)
+// the chunk's own exact top K comes from an MSD radix select.  dense_finish
+// combines the partial sums into the LogSoftmax constant and writes ids,
+// scores and gates sorted by (score desc, id asc).
 
 #include "omni_internal.h"
 
@@ -27,7 +22,9 @@ namespace omni {
 namespace {
 
 constexpr int DR_THREADS = 256;
-constexpr int DR_CAP = 2048;  // LDS buffer of boundary-bucket keys
+constexpr int DR_CAP = 2048;  // LDS buffer of boundary-bucket keys / survivors
+static_assert(DR_CAP >= OMNI_MAX_K && (DR_CAP & (DR_CAP - 1)) == 0,
+              "the merge pads DR_CAP + OMNI_MAX_K keys to at most 2 * DR_CAP");
 constexpr int DR_BINS = 2048;
 
 typedef unsigned long long u64;
@@ -74,69 +71,23 @@ __device__ void dr_sort_desc(u64* a, int n) {
   __syncthreads();
 }
 
-// CHUNK: vals = this chunk's logits (ids id0 + i); writes K candidate
-// (value, id) pairs (unsorted; padded with -inf when n < K) and the chunk's
-// (max, sum exp(v - max)) to part[t * nparts + slot].
-// FINAL: vals/ids = the token's candidates from every chunk; combines the
-// nparts partials into lse and writes idx, score = v - lse and gate =
-// softmax over the selected, sorted by (score desc, id asc).
-// Selection runs on the 64-bit keys (value order, then smaller id), which are
-// distinct, so refining the boundary bucket always ends with at most DR_CAP
-// keys in it.
-template <bool FINAL>
-__global__ __launch_bounds__(DR_THREADS) void dense_select(
-    const float* __restrict__ vals, const int32_t* __restrict__ ids, int n, int ld, int id0,
-    int K, int nparts, int slot, float* __restrict__ cand_v, int32_t* __restrict__ cand_i,
-    int cand_ld, float2* __restrict__ part, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, float* __restrict__ gate_out) {
-  __shared__ int hist[DR_BINS];
-  __shared__ u64 buf[DR_CAP];
-  __shared__ u64 sel[OMNI_MAX_K];
-  __shared__ int red[DR_THREADS / 64];
-  __shared__ float redf[2 * (DR_THREADS / 64)];
-  __shared__ int s_nsel, s_nbuf, s_bucket, s_above;
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const float* row = vals + (size_t)t * ld;
-  const int32_t* irow = FINAL ? ids + (size_t)t * ld : nullptr;
-  auto key_of = [&](int i) -> u64 {
-    const unsigned id = FINAL ? (unsigned)irow[i] : (unsigned)(id0 + i);
-    return dr_key(float_ord(row[i]), id);
-  };
-
-  // ---- level 0: 11-bit histogram of key bits 63..53 (+ online max and sum
-  //      of exp in chunk mode)
+// Exact top-K keys of row[0..n) (ids id0 + i), by an MSD radix select over
+// the 64-bit keys: level 0 is an 11-bit histogram of the key's top bits,
+// further digits refine the boundary bucket while it holds more than DR_CAP
+// keys, then one pass collects the keys above the bucket into sel and the
+// bucket into buf, which is sorted exactly.  Leaves min(K, n) keys in sel
+// (unsorted) and returns their number.  Whole-workgroup call.
+__device__ int dr_radix_topk(const float* row, int n, int id0, int K, int* hist, u64* buf,
+                             u64* sel, int* red, int* sh) {
+  const int tid = threadIdx.x;
+  auto key_of = [&](int i) -> u64 { return dr_key(float_ord(row[i]), (unsigned)(id0 + i)); };
   for (int b = tid; b < DR_BINS; b += DR_THREADS) hist[b] = 0;
   __syncthreads();
-  float m = -INFINITY, se = 0.f;
-  for (int i = tid; i < n; i += DR_THREADS) {
-    const float v = row[i];
-    atomicAdd(&hist[float_ord(v) >> 21], 1);
-    if constexpr (!FINAL) {
-      if (v > m) {
-        se = se * expf(m - v) + 1.f;
-        m = v;
-      } else {
-        se += expf(v - m);
-      }
-    }
-  }
-  if constexpr (!FINAL) {
-    const float wm = wave_max(m);
-    float sw = (m == -INFINITY) ? 0.f : se * expf(m - wm);
-    sw = wave_sum(sw);
-    const int w = tid >> 6;
-    if ((tid & 63) == 0) {
-      redf[2 * w] = wm;
-      redf[2 * w + 1] = sw;
-    }
-  }
+  for (int i = tid; i < n; i += DR_THREADS) atomicAdd(&hist[float_ord(row[i]) >> 21], 1);
   __syncthreads();
-
-  // ---- boundary bucket: count(keys in higher buckets) < K - above <= count(>= it);
-  //      refine with the next digit while the bucket overflows the buffer
   u64 prefix = 0;  // key bits above `shift`
   int shift = 53, width = 11, above = 0, cnt_b = 0;
-  bool all = false;  // fewer than K keys in total: take them all
+  bool all = false;  // fewer than K keys: take them all
   for (;;) {
     const int nb = 1 << width;
     const int per = (nb + DR_THREADS - 1) / DR_THREADS;
@@ -149,7 +100,7 @@ __global__ __launch_bounds__(DR_THREADS) void dense_select(
     const int ex = dr_block_excl(local, red, &total);
     const int from_me = total - ex;  // keys in bins >= tid * per
     const int need = K - above;
-    if (tid == 0) s_bucket = -1;
+    if (tid == 0) sh[0] = -1;
     __syncthreads();
     if (from_me >= need && from_me - local < need) {
       int run = from_me - local;
@@ -157,20 +108,20 @@ __global__ __launch_bounds__(DR_THREADS) void dense_select(
         const int b = tid * per + q;
         const int c = b < nb ? hist[b] : 0;
         if (run + c >= need) {
-          s_bucket = b;
-          s_above = run;
+          sh[0] = b;
+          sh[1] = run;
           break;
         }
         run += c;
       }
     }
     __syncthreads();
-    if (s_bucket < 0) {
+    if (sh[0] < 0) {
       all = true;
       break;
     }
-    const int bucket = s_bucket;
-    above += s_above;
+    const int bucket = sh[0];
+    above += sh[1];
     cnt_b = hist[bucket];
     prefix = (prefix << width) | (u64)bucket;
     if (cnt_b <= DR_CAP || shift == 0) break;
@@ -181,84 +132,161 @@ __global__ __launch_bounds__(DR_THREADS) void dense_select(
     __syncthreads();
     for (int i = tid; i < n; i += DR_THREADS) {
       const u64 k = key_of(i);
-      if ((k >> shift) == prefix) atomicAdd(&hist[(int)((k >> nshift) & ((1ull << nwidth) - 1ull))], 1);
+      if ((k >> shift) == prefix)
+        atomicAdd(&hist[(int)((k >> nshift) & ((1ull << nwidth) - 1ull))], 1);
     }
     __syncthreads();
     shift = nshift;
     width = nwidth;
   }
-
-  // ---- collect: keys above the boundary bucket into sel, the bucket into buf
   if (tid == 0) {
-    s_nsel = 0;
-    s_nbuf = 0;
+    sh[2] = 0;
+    sh[3] = 0;
   }
   __syncthreads();
   for (int i = tid; i < n; i += DR_THREADS) {
     const u64 k = key_of(i);
     const u64 top = k >> shift;
     if (all || top > prefix) {
-      sel[atomicAdd(&s_nsel, 1)] = k;
+      sel[atomicAdd(&sh[2], 1)] = k;
     } else if (top == prefix) {
-      buf[atomicAdd(&s_nbuf, 1)] = k;
+      buf[atomicAdd(&sh[3], 1)] = k;
     }
   }
   __syncthreads();
-  int nsel = s_nsel;
-  if (!all) {
-    const int need = K - nsel;
-    int nb = 1;
-    while (nb < cnt_b) nb <<= 1;
-    for (int i = cnt_b + tid; i < nb; i += DR_THREADS) buf[i] = 0ull;
-    dr_sort_desc(buf, nb);
-    for (int i = tid; i < need; i += DR_THREADS) sel[nsel + i] = buf[i];
-    nsel = K;
-  }
+  const int nsel = sh[2];
+  if (all) return nsel;
+  int nb = 1;
+  while (nb < cnt_b) nb <<= 1;
+  for (int i = cnt_b + tid; i < nb; i += DR_THREADS) buf[i] = 0ull;
+  dr_sort_desc(buf, nb);
+  for (int i = tid; i < K - nsel; i += DR_THREADS) sel[nsel + i] = buf[i];
   __syncthreads();
+  return K;
+}
 
-  if constexpr (!FINAL) {
-    for (int i = tid; i < K; i += DR_THREADS) {
-      const u64 k = i < nsel ? sel[i] : 0ull;
-      cand_v[(size_t)t * cand_ld + i] = i < nsel ? ord_float((unsigned)(k >> 32)) : -INFINITY;
-      cand_i[(size_t)t * cand_ld + i] = i < nsel ? (int32_t)(~(unsigned)k) : 0;
+// One chunk of experts for every token (one workgroup per token).  state[t]
+// holds the token's K best keys so far, sorted descending (slot 0: none).
+// One pass over the chunk's logits (16-byte loads) accumulates the chunk's
+// (max, sum exp(v - max)) into part[t * nparts + slot] and collects the keys
+// above the token's current K-th key; if more than DR_CAP pass (always on
+// the first chunk), the chunk's own top K is taken by dr_radix_topk instead.
+// The survivors and the old state are merged, sorted, and the first K kept.
+__global__ __launch_bounds__(DR_THREADS) void dense_chunk(const float* __restrict__ vals, int n,
+                                                          int ld, int id0, int K, int slot,
+                                                          int nparts, u64* __restrict__ state,
+                                                          float2* __restrict__ part) {
+  __shared__ int hist[DR_BINS];
+  // survivors (<= DR_CAP) + the old state (<= OMNI_MAX_K), padded to a power
+  // of two for the sort
+  __shared__ u64 buf[2 * DR_CAP];
+  __shared__ u64 sel[OMNI_MAX_K];
+  __shared__ int red[DR_THREADS / 64];
+  __shared__ float redf[2 * (DR_THREADS / 64)];
+  __shared__ int sh[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* row = vals + (size_t)t * ld;
+  u64* st = state + (size_t)t * K;
+  const u64 T = slot == 0 ? 0ull : st[K - 1];  // keys must exceed the K-th best so far
+  if (tid == 0) sh[2] = 0;
+  __syncthreads();
+  float m = -INFINITY, se = 0.f;
+  auto visit = [&](float v, int i) {
+    if (v > m) {
+      se = se * expf(m - v) + 1.f;
+      m = v;
+    } else {
+      se += expf(v - m);
     }
-    if (tid == 0) {
-      float M = -INFINITY;
-      for (int w = 0; w < DR_THREADS / 64; ++w) M = fmaxf(M, redf[2 * w]);
-      float S = 0.f;
-      for (int w = 0; w < DR_THREADS / 64; ++w)
-        if (redf[2 * w] > -INFINITY) S += redf[2 * w + 1] * expf(redf[2 * w] - M);
-      part[(size_t)t * nparts + slot] = make_float2(M, S);
+    const u64 k = dr_key(float_ord(v), (unsigned)(id0 + i));
+    if (k > T) {
+      const int p = atomicAdd(&sh[2], 1);
+      if (p < DR_CAP) buf[p] = k;
     }
-  } else {
-    int nk = 1;
-    while (nk < K) nk <<= 1;
-    for (int i = tid; i < nk; i += DR_THREADS) buf[i] = i < K ? sel[i] : 0ull;
-    dr_sort_desc(buf, nk);
-    if (tid == 0) {
-      float M = -INFINITY;
-      for (int c = 0; c < nparts; ++c) M = fmaxf(M, part[(size_t)t * nparts + c].x);
-      float S = 0.f;
-      for (int c = 0; c < nparts; ++c) {
-        const float2 pc = part[(size_t)t * nparts + c];
-        if (pc.x > -INFINITY) S += pc.y * expf(pc.x - M);
-      }
-      const float top = ord_float((unsigned)(buf[0] >> 32));
-      float z = 0.f;
-      for (int k = 0; k < K; ++k) z += expf(ord_float((unsigned)(buf[k] >> 32)) - top);
-      redf[0] = M + logf(S);
-      redf[1] = z;
-      redf[2] = top;
+  };
+  const bool vec = ((ld & 3) == 0) && ((((uintptr_t)vals) & 15) == 0);
+  int i0 = 0;
+  if (vec) {
+    for (int i = 4 * tid; i + 3 < n; i += 4 * DR_THREADS) {
+      const f32x4 f = *(const f32x4*)(row + i);
+      visit(f[0], i);
+      visit(f[1], i + 1);
+      visit(f[2], i + 2);
+      visit(f[3], i + 3);
     }
+    i0 = n & ~3;
+  }
+  for (int i = i0 + tid; i < n; i += DR_THREADS) visit(row[i], i);
+  {
+    const float wm = wave_max(m);
+    float sw = (m == -INFINITY) ? 0.f : se * expf(m - wm);
+    sw = wave_sum(sw);
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) {
+      redf[2 * w] = wm;
+      redf[2 * w + 1] = sw;
+    }
+  }
+  __syncthreads();
+  int nnew = sh[2];
+  if (nnew > DR_CAP) {  // too many survivors: the chunk's exact top K
+    nnew = dr_radix_topk(row, n, id0, K, hist, buf, sel, red, sh);
+    for (int i = tid; i < nnew; i += DR_THREADS) buf[i] = sel[i];
     __syncthreads();
-    const float lse = redf[0], z = redf[1], top = redf[2];
-    for (int k = tid; k < K; k += DR_THREADS) {
-      const u64 key = buf[k];
-      const float v = ord_float((unsigned)(key >> 32));
-      idx_out[(size_t)t * K + k] = (int32_t)(~(unsigned)key);
-      score_out[(size_t)t * K + k] = v - lse;
-      gate_out[(size_t)t * K + k] = expf(v - top) / z;
+  }
+  // merge with the previous state, keep the best K (sorted)
+  const int nold = slot == 0 ? 0 : K;
+  for (int i = tid; i < nold; i += DR_THREADS) buf[nnew + i] = st[i];
+  const int tot = nnew + nold;
+  int nb = 1;
+  while (nb < tot) nb <<= 1;
+  for (int i = tot + tid; i < nb; i += DR_THREADS) buf[i] = 0ull;
+  dr_sort_desc(buf, nb);
+  for (int i = tid; i < K; i += DR_THREADS) st[i] = i < tot ? buf[i] : 0ull;
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int w = 0; w < DR_THREADS / 64; ++w) M = fmaxf(M, redf[2 * w]);
+    float S = 0.f;
+    for (int w = 0; w < DR_THREADS / 64; ++w)
+      if (redf[2 * w] > -INFINITY) S += redf[2 * w + 1] * expf(redf[2 * w] - M);
+    part[(size_t)t * nparts + slot] = make_float2(M, S);
+  }
+}
+
+// lse from the chunk partials; ids, scores p = s - lse and gates (softmax
+// over the K selected) from the final state (already sorted).
+__global__ __launch_bounds__(DR_THREADS) void dense_finish(const u64* __restrict__ state,
+                                                           const float2* __restrict__ part,
+                                                           int nparts, int K,
+                                                           int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ score_out,
+                                                           float* __restrict__ gate_out) {
+  __shared__ float redf[3];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const u64* st = state + (size_t)t * K;
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int c = 0; c < nparts; ++c) M = fmaxf(M, part[(size_t)t * nparts + c].x);
+    float S = 0.f;
+    for (int c = 0; c < nparts; ++c) {
+      const float2 pc = part[(size_t)t * nparts + c];
+      if (pc.x > -INFINITY) S += pc.y * expf(pc.x - M);
     }
+    const float top = ord_float((unsigned)(st[0] >> 32));
+    float z = 0.f;
+    for (int k = 0; k < K; ++k) z += expf(ord_float((unsigned)(st[k] >> 32)) - top);
+    redf[0] = M + logf(S);
+    redf[1] = z;
+    redf[2] = top;
+  }
+  __syncthreads();
+  const float lse = redf[0], z = redf[1], top = redf[2];
+  for (int k = tid; k < K; k += DR_THREADS) {
+    const u64 key = st[k];
+    const float v = ord_float((unsigned)(key >> 32));
+    idx_out[(size_t)t * K + k] = (int32_t)(~(unsigned)key);
+    score_out[(size_t)t * K + k] = v - lse;
+    gate_out[(size_t)t * K + k] = expf(v - top) / z;
   }
 }
 
@@ -275,8 +303,7 @@ DenseRouterPlan plan_dense_router(int64_t L, int64_t N, int64_t K) {
     return at;
   };
   p.off_logits = take((size_t)L * p.chunk * 4);
-  p.off_cand_v = take((size_t)L * p.nchunks * K * 4);
-  p.off_cand_i = take((size_t)L * p.nchunks * K * 4);
+  p.off_state = take((size_t)L * K * 8);
   p.off_part = take((size_t)L * p.nchunks * 8);
   p.ws_bytes = o;
   return p;
@@ -287,10 +314,8 @@ hipError_t launch_dense_router(const void* x, const void* Wn, int L, int d, int 
                                const DenseRouterPlan& p, void* ws, hipStream_t s) {
   char* w = (char*)ws;
   float* logits = (float*)(w + p.off_logits);
-  float* cand_v = (float*)(w + p.off_cand_v);
-  int32_t* cand_i = (int32_t*)(w + p.off_cand_i);
+  u64* state = (u64*)(w + p.off_state);
   float2* part = (float2*)(w + p.off_part);
-  const int cand_ld = p.nchunks * K;
   hipError_t e;
   for (int c = 0; c < p.nchunks; ++c) {
     const int c0 = c * p.chunk;
@@ -303,16 +328,11 @@ hipError_t launch_dense_router(const void* x, const void* Wn, int L, int d, int 
       const float* Wc = (const float*)Wn + (size_t)c0 * d;
       if ((e = gemm_f32((const float*)x, d, 1, Wc, d, 1, L, nc, d, logits, nc, false, s))) return e;
     }
-    // chunk c's candidates go to columns [c*K, c*K + K) of the candidate rows;
-    // its partial sums to part[t * nchunks + c]
-    hipLaunchKernelGGL(dense_select<false>, dim3(L), dim3(DR_THREADS), 0, s, logits,
-                       (const int32_t*)nullptr, nc, nc, c0, K, p.nchunks, c,
-                       cand_v + (size_t)c * K, cand_i + (size_t)c * K, cand_ld, part,
-                       (int32_t*)nullptr, (float*)nullptr, (float*)nullptr);
+    hipLaunchKernelGGL(dense_chunk, dim3(L), dim3(DR_THREADS), 0, s, logits, nc, nc, c0, K, c,
+                       p.nchunks, state, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(dense_select<true>, dim3(L), dim3(DR_THREADS), 0, s, cand_v, cand_i, cand_ld,
-                     cand_ld, 0, K, p.nchunks, 0, (float*)nullptr, (int32_t*)nullptr, 0, part,
+  hipLaunchKernelGGL(dense_finish, dim3(L), dim3(DR_THREADS), 0, s, state, part, p.nchunks, K,
                      idx, score, gate);
   return hipGetLastError();
 }

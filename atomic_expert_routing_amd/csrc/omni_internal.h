@@ -177,7 +177,7 @@ hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act
 constexpr int DENSE_ROUTER_CHUNK = 65536;  // experts per logits chunk
 struct DenseRouterPlan {
   int chunk, nchunks;
-  size_t off_logits, off_cand_v, off_cand_i, off_part, ws_bytes;
+  size_t off_logits, off_state, off_part, ws_bytes;
 };
 DenseRouterPlan plan_dense_router(int64_t L, int64_t N, int64_t K);
 hipError_t launch_dense_router(const void* x, const void* Wn, int L, int d, int N, int K,

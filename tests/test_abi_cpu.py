@@ -172,11 +172,11 @@ def test_shared_mlp_workspace_and_validation():
 
 
 def test_dense_router_workspace_and_validation():
-    # chunk logits [L, 65536] fp32 + candidates (value, id) [L, chunks*K] + partials
+    # chunk logits [L, 65536] fp32 + running top-K keys [L, K] u64 + partials
     L, N, K = 4096, 1700416, 128
     chunks = -(-N // 65536)
     ws = omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=L, d=2048, K=K, N=N)
-    assert ws == L * 65536 * 4 + 2 * L * chunks * K * 4 + L * chunks * 8
+    assert ws == L * 65536 * 4 + L * K * 8 + L * chunks * 8
     small = omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=8, d=64, K=4, N=100)
     assert small >= 8 * 100 * 4
     for kw, st in ((dict(K=101, N=100), omni.OMNI_ERR_INVALID_ARG),
