@@ -345,3 +345,24 @@ class RoutedBranch:
         self.router(x, Wr, Wc, stream)
         self.schedule(stream)
         return self.expert_forward(x, W, V, stream)
+
+    def capture(self, x, Wr, Wc, W, V):
+        """Record one forward (router, schedule, assembly) as a HIP graph over
+        these input tensors and this instance's buffers; replay() reruns it.
+        The library allocates nothing and issues no memset, so the three
+        calls capture as plain kernel nodes."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside the capture
+            self.forward(x, Wr, Wc, W, V)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.forward(x, Wr, Wc, W, V)
+        torch.cuda.synchronize()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()
+        return self.y

@@ -12,6 +12,11 @@ arithmetic).  Prints ONE JSON line.
 Timing: W untimed steps, then exactly K steps between two device
 synchronisations (wall clock), with HIP events (torch.cuda.Event on the
 stream the library launches on) around each call for the per-stage split.
+Then the same step is captured once as a HIP graph (the three calls'
+kernels, on preallocated buffers) and W + K replays are timed the same way
+(graph_ms_per_step; --graph makes it the value).  Measured on MI355X the
+replays are about 1.5% slower than eager launches, which already keep the
+GPU busy, so the eager rate is the value by default.
 The roofline entry covers the expert-assembly call (its two kernels:
 expert_act and expert_out), whose algorithmic bytes are the unique W and V
 rows gathered, x read once, y written once and 12 bytes of task metadata
@@ -56,6 +61,9 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MB "
                          "Infinity Cache, timed with events (0 to skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="report replays of the step captured as a HIP graph as the value "
+                         "(both rates are always given)")
     ap.add_argument("--no-dense-router", action="store_true",
                     help="skip timing the fully connected router of the ablation")
     ap.add_argument("--no-backward", action="store_true",
@@ -336,14 +344,27 @@ def main():
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} eager steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = eager_ms
+    # the same step captured once as a HIP graph and replayed
+    br.capture(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    for _ in range(args.warmup):
+        br.replay()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} graph replays")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        br.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if args.graph:
+        ms_step = graph_ms
 
     def med(a, b):
         return statistics.median(e[a].elapsed_time(e[b]) for e in evs)
@@ -378,6 +399,10 @@ def main():
         "data": "synthetic: seeded Gaussian x and random-init W, V, W_r, W_c (no trained weights)",
         "config": {**w.describe(), "parallelism": "single GPU"},
         "tokens_per_s": round(w.L / (ms_step * 1e-3), 1),
+        "timing": "replays of the step captured as a HIP graph" if args.graph
+                  else "eager launches",
+        "eager_ms_per_step": round(eager_ms, 4),
+        "graph_ms_per_step": round(graph_ms, 4),
         "branch_hbm_frac": round(branch_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "stages_ms_median": {"router": round(router_ms, 4), "schedule": round(sched_ms, 4),
                              "expert_forward": round(expert_ms, 4),
