@@ -170,28 +170,35 @@ omni_status omni_router(const void* x, const void* Wr, const void* Wc, int64_t L
 }
 
 omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K, int64_t N, int64_t B,
-                          int32_t* perm, int32_t* group_off, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          int32_t* perm, int32_t* group_off, int32_t* token_order, void* ws,
+                          size_t ws_bytes, void* stream) {
   size_t need = 0;
   omni_status s = schedule_ws(L, K, N, B, &need);
   if (s != OMNI_OK) return s;
   if (!idx || !perm || !group_off) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL array pointer");
+  if (token_order && L > I32_LIMIT - 7)
+    return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
   const omni::SchedPlan plan = omni::plan_schedule(L, K, N, B);
-  hipError_t e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws,
-                                       (hipStream_t)stream);
-  return hip_status(e, "schedule launch");
+  hipError_t e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws, st);
+  if (e != hipSuccess || !token_order) return hip_status(e, "schedule launch");
+  e = omni::launch_token_order(idx, (int)L, (int)K, N, (int)B, token_order, ws, st);
+  return hip_status(e, "token order launch");
 }
 
 omni_status omni_expert_forward(const void* x, const void* W, const void* V, const int32_t* idx,
-                                const float* gate, const int32_t* perm, int64_t L, int64_t d,
-                                int64_t N, int64_t K, omni_dtype dt, float* y, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                const float* gate, const int32_t* perm,
+                                const int32_t* token_order, int64_t L, int64_t d, int64_t N,
+                                int64_t K, omni_dtype dt, float* y, void* ws, size_t ws_bytes,
+                                void* stream) {
   size_t need = 0;
   omni_status s = expert_ws(L, d, N, K, dt, &need);
   if (s != OMNI_OK) return s;
   if (!x || !W || !V || !idx || !gate || !perm || !y)
     return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: NULL array pointer");
+  if (token_order && L > I32_LIMIT - 7)
+    return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
   if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(y))
     return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: x, W, V and y must be 16-byte aligned");
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
@@ -199,7 +206,7 @@ omni_status omni_expert_forward(const void* x, const void* W, const void* V, con
   float* act = (float*)ws;
   hipError_t e = omni::launch_expert_act(x, W, idx, gate, perm, (int)L, (int)d, (int)K, dt, act, st);
   if (e != hipSuccess) return hip_status(e, "expert activation launch");
-  e = omni::launch_expert_out(V, idx, act, (int)L, (int)d, (int)K, dt, y, st);
+  e = omni::launch_expert_out(V, idx, act, token_order, (int)L, (int)d, (int)K, dt, y, st);
   return hip_status(e, "expert output launch");
 }
 

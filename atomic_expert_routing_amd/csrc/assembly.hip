@@ -171,18 +171,33 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
 // staged in LDS once; each thread owns 16 bytes of y's row and streams the
 // K rows of V, OUT_UNROLL row loads in flight (kept together by a
 // scheduling barrier), then accumulates them in k order.
+//
+// With a token order, the grid has 8 * ceil(L/8) slots and workgroup b
+// (which runs on XCD b % 8) takes slot (b % 8) * ceil(L/8) + b / 8: each XCD
+// walks its own contiguous eighth of the order, so tokens that the order
+// puts together share that XCD's L2.  Slots past L and entries outside
+// [0, L) do nothing.
 constexpr int OUT_UNROLL = 16;
 
 template <bool BF16>
 __global__ __launch_bounds__(512) void expert_out(const uint16_t* __restrict__ V_,
                                                   const int32_t* __restrict__ idx,
-                                                  const float* __restrict__ act, int d, int K,
-                                                  float* __restrict__ y) {
+                                                  const float* __restrict__ act,
+                                                  const int32_t* __restrict__ order, int L, int d,
+                                                  int K, float* __restrict__ y) {
   using V = Vec<BF16>;
   constexpr int E = V::E;
   __shared__ int se[OMNI_MAX_K];
   __shared__ float sa[OMNI_MAX_K];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  int t = blockIdx.x;
+  if (order) {
+    const int per = (L + 7) / 8;
+    const int slot = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (slot >= L) return;
+    t = order[slot];
+    if ((unsigned)t >= (unsigned)L) return;
+  }
+  const int tid = threadIdx.x;
   for (int k = tid; k < K; k += blockDim.x) {
     se[k] = idx[(size_t)t * K + k];
     sa[k] = act[(size_t)t * K + k];
@@ -358,15 +373,18 @@ hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const i
                          : launch_tc_t<false>(x, W, V, idx, gate, L, d, K, y, s);
 }
 
-hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,
-                             int K, omni_dtype dt, float* y, hipStream_t s) {
+hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act,
+                             const int32_t* order, int L, int d, int K, omni_dtype dt, float* y,
+                             hipStream_t s) {
   const int E = dt == OMNI_BF16 ? 8 : 4;
   const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
-  const dim3 grid(L), block(threads);
+  const dim3 grid(order ? 8 * ((L + 7) / 8) : L), block(threads);
   if (dt == OMNI_BF16)
-    hipLaunchKernelGGL(expert_out<true>, grid, block, 0, s, (const uint16_t*)V, idx, act, d, K, y);
+    hipLaunchKernelGGL(expert_out<true>, grid, block, 0, s, (const uint16_t*)V, idx, act, order, L,
+                       d, K, y);
   else
-    hipLaunchKernelGGL(expert_out<false>, grid, block, 0, s, (const uint16_t*)V, idx, act, d, K, y);
+    hipLaunchKernelGGL(expert_out<false>, grid, block, 0, s, (const uint16_t*)V, idx, act, order,
+                       L, d, K, y);
   return hipGetLastError();
 }
 

@@ -160,6 +160,11 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
                            int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
+// order[0..L) = the tokens stably sorted by idx[t*K] / B (the group of each
+// token's first expert); uses the schedule's workspace (plan_schedule(L, K, ..)
+// covers it)
+hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
+                              int32_t* order, void* ws, hipStream_t s);
 
 // act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order
 hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, const float* gate,
@@ -169,9 +174,11 @@ hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, c
 hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,
                             const float* gate, int L, int d, int K, omni_dtype dt, float* y,
                             hipStream_t s);
-// y[t] = sum_k act[t*K+k] * V[idx[t*K+k]]
-hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act, int L, int d,
-                             int K, omni_dtype dt, float* y, hipStream_t s);
+// y[t] = sum_k act[t*K+k] * V[idx[t*K+k]]; tokens visited in `order` (a
+// permutation of [0, L), XCD x taking its x-th eighth) or, if null, by id
+hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act,
+                             const int32_t* order, int L, int d, int K, omni_dtype dt, float* y,
+                             hipStream_t s);
 
 // ----------------------------------------------------------------- dense router
 constexpr int DENSE_ROUTER_CHUNK = 65536;  // experts per logits chunk

@@ -14,6 +14,10 @@
 //   sched_scatter  stable scatter: in-tile ranks from wave ballots
 // followed by sched_offsets, which turns the sorted group ids into
 // group_off[q] = first sorted position whose group is >= q.
+//
+// The same sort, over the L tokens keyed by the group of each token's first
+// expert, gives the token order the output pass may follow: tokens whose
+// leading experts coincide run next to each other (and on one XCD).
 
 #include "omni_internal.h"
 
@@ -24,14 +28,18 @@ constexpr int SCHED_THREADS = 256;
 constexpr int SCHED_ROUNDS = 8;  // elements per tile = 256 * 8
 constexpr int SCHED_TILE = SCHED_THREADS * SCHED_ROUNDS;
 
+// Element p's key: its group, idx[p * stride] / B, in the first pass; the
+// previous pass's sorted key afterwards.
 __device__ __forceinline__ int load_key(const int32_t* __restrict__ idx,
-                                        const int32_t* __restrict__ keys_in, int p, int B) {
-  return keys_in ? keys_in[p] : idx[p] / B;
+                                        const int32_t* __restrict__ keys_in, int p, int stride,
+                                        int B) {
+  return keys_in ? keys_in[p] : idx[(size_t)p * stride] / B;
 }
 
 __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ keys_in,
-                                                            int M, int B, int shift, int radix,
+                                                            int M, int stride, int B, int shift,
+                                                            int radix,
                                                             int ntiles, int* __restrict__ hist) {
   __shared__ int h[256];
   const int tid = threadIdx.x, tile = blockIdx.x;
@@ -40,7 +48,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __res
   const int base = tile * SCHED_TILE;
   for (int r = 0; r < SCHED_ROUNDS; ++r) {
     const int p = base + r * SCHED_THREADS + tid;
-    if (p < M) atomicAdd(&h[(load_key(idx, keys_in, p, B) >> shift) & (radix - 1)], 1);
+    if (p < M) atomicAdd(&h[(load_key(idx, keys_in, p, stride, B) >> shift) & (radix - 1)], 1);
   }
   __syncthreads();
   if (tid < radix) hist[tid * ntiles + tile] = h[tid];
@@ -85,7 +93,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(int* __restri
 
 __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
-    const int32_t* __restrict__ vals_in, int M, int B, int shift, int radix, int ntiles,
+    const int32_t* __restrict__ vals_in, int M, int stride, int B, int shift, int radix,
+    int ntiles,
     const int* __restrict__ hist, const int* __restrict__ totals, int32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out) {
   __shared__ int run[256];
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
     const bool act = p < M;
     int key = 0, val = 0, dig = 0;
     if (act) {
-      key = load_key(idx, keys_in, p, B);
+      key = load_key(idx, keys_in, p, stride, B);
       val = vals_in ? vals_in[p] : p;
       dig = (key >> shift) & (radix - 1);
     }
@@ -197,8 +206,13 @@ const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws) {
   return (const int32_t*)(w + (((plan.passes - 1) & 1) ? plan.off_keys_b : plan.off_keys_a));
 }
 
-hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
+namespace {
+
+// Stable LSD sort of the elements p < M by group idx[p * stride] / B; the
+// last pass writes the element indices in sorted order to `vals_last` and
+// leaves the sorted keys in the workspace.
+void sort_by_group(const int32_t* idx, int stride, int M, int B, const SchedPlan& plan,
+                   int32_t* vals_last, void* ws, hipStream_t s) {
   char* w = (char*)ws;
   int32_t* ka = (int32_t*)(w + plan.off_keys_a);
   int32_t* va = (int32_t*)(w + plan.off_vals_a);
@@ -208,23 +222,38 @@ hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedP
   int* totals = (int*)(w + plan.off_totals);
   const int radix = 1 << plan.digit_bits;
   const int32_t* kin = nullptr;  // pass 0 derives keys from idx
-  const int32_t* vin = nullptr;  // pass 0 values are the task ids
+  const int32_t* vin = nullptr;  // pass 0 values are the element ids
   for (int pass = 0; pass < plan.passes; ++pass) {
     const bool last = pass + 1 == plan.passes;
     int32_t* kout = (pass & 1) ? kb : ka;
-    int32_t* vout = last ? perm : ((pass & 1) ? vb : va);
+    int32_t* vout = last ? vals_last : ((pass & 1) ? vb : va);
     const int shift = pass * plan.digit_bits;
-    hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M, B,
-                       shift, radix, plan.ntiles, hist);
+    hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M,
+                       stride, B, shift, radix, plan.ntiles, hist);
     hipLaunchKernelGGL(sched_scan_digits, dim3(radix), dim3(SCHED_THREADS), 0, s, hist,
                        plan.ntiles, totals);
     hipLaunchKernelGGL(sched_scatter, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, vin,
-                       M, B, shift, radix, plan.ntiles, hist, totals, kout, vout);
+                       M, stride, B, shift, radix, plan.ntiles, hist, totals, kout, vout);
     kin = kout;
     vin = vout;
   }
-  hipLaunchKernelGGL(sched_offsets, dim3((M + 1 + 255) / 256), dim3(256), 0, s, kin, M, G,
-                     group_off);
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
+  sort_by_group(idx, 1, M, B, plan, perm, ws, s);
+  hipLaunchKernelGGL(sched_offsets, dim3((M + 1 + 255) / 256), dim3(256), 0, s,
+                     schedule_sorted_keys(plan, ws), M, G, group_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
+                              int32_t* order, void* ws, hipStream_t s) {
+  // the plan for L elements needs no more workspace than the one for L*K
+  const SchedPlan plan = plan_schedule(L, 1, N, B);
+  sort_by_group(idx, K, L, B, plan, order, ws, s);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 4
+_ABI_VERSION = 5
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
@@ -51,8 +51,8 @@ def library() -> ctypes.CDLL:
     i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     lib.omni_router.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
                                 vp, vp, vp, vp, sz, vp]
-    lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
-    lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+    lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                       ctypes.c_int, vp, vp]
@@ -158,8 +158,14 @@ def omni_router(x, Wr, Wc, K: int, idx=None, score=None, gate=None, ws=None, str
     return idx, score, gate
 
 
-def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, stream=None):
-    """Expert-centric schedule -> (perm [L*K] int32, group_off [G+1] int32)."""
+def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, stream=None,
+                  token_order=None):
+    """Expert-centric schedule -> (perm [L*K] int32, group_off [G+1] int32).
+
+    token_order: None (not computed), True (allocate) or an [L] int32 tensor;
+    when given, the tokens sorted by the group of their first expert are
+    written there and returned as a third element.
+    """
     L, K = idx.shape
     G = -(-N // B)
     pi = _dev(idx, "idx", torch.int32)
@@ -169,14 +175,21 @@ def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, strea
     pp = _dev(perm, "perm", torch.int32, (L * K,))
     po = _dev(group_off, "group_off", torch.int32, (G + 1,))
     need = omni_workspace_bytes(OMNI_OP_SCHEDULE, L, 8, 1, 1, K, N, B) if ws is None else 0
+    if token_order is True:
+        token_order = torch.empty((L,), **kw)
+    pt = None if token_order is None else _dev(token_order, "token_order", torch.int32, (L,))
     pw, nw = _workspace(ws, need, idx.device)
-    _check(library().omni_schedule(pi, L, K, N, B, pp, po, pw, nw, _stream(stream)),
+    _check(library().omni_schedule(pi, L, K, N, B, pp, po, pt, pw, nw, _stream(stream)),
            "omni_schedule")
-    return perm, group_off
+    return (perm, group_off) if token_order is None else (perm, group_off, token_order)
 
 
-def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None):
-    """Dynamic Expert Assembly over the schedule -> y [L, d] float32."""
+def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None,
+                        token_order=None):
+    """Dynamic Expert Assembly over the schedule -> y [L, d] float32.
+
+    token_order (optional [L] int32, from omni_schedule) sets the order in
+    which the output pass visits tokens; y does not depend on it."""
     L, d = x.shape
     N = W.shape[0]
     K = idx.shape[1]
@@ -187,11 +200,12 @@ def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None):
     pi = _dev(idx, "idx", torch.int32, (L, K))
     pg = _dev(gate, "gate", torch.float32, (L, K))
     pp = _dev(perm, "perm", torch.int32, (L * K,))
+    pt = None if token_order is None else _dev(token_order, "token_order", torch.int32, (L,))
     y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
     py = _dev(y, "y", torch.float32, (L, d))
     need = omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
     pw, nw = _workspace(ws, need, x.device)
-    _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, L, d, N, K, dt, py, pw, nw,
+    _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, pt, L, d, N, K, dt, py, pw, nw,
                                          _stream(stream)), "omni_expert_forward")
     return y
 
@@ -310,10 +324,15 @@ class RoutedBranch:
     """Preallocated outputs and workspaces for repeated routed-branch forwards.
 
     One instance per (shape, dtype): `forward(x, Wr, Wc, W, V)` enqueues the
-    three C calls on the current stream and allocates nothing.
+    three C calls on the current stream and allocates nothing.  With
+    token_order=True the schedule also sorts the tokens by their first
+    expert's group and the output pass follows that order: it pays where
+    tokens pile onto few experts (clustered routing) and costs a little on
+    spread-out routing.
     """
 
-    def __init__(self, L, d, Nr, Nc, K, B, dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, L, d, Nr, Nc, K, B, dtype=torch.bfloat16, device="cuda",
+                 token_order=False):
         self.L, self.d, self.Nr, self.Nc, self.K, self.B = L, d, Nr, Nc, K, B
         self.N = Nr * Nc
         self.G = -(-self.N // B)
@@ -326,6 +345,7 @@ class RoutedBranch:
         self.perm = torch.empty((L * K,), dtype=i32, **kw)
         self.group_off = torch.empty((self.G + 1,), dtype=i32, **kw)
         self.y = torch.empty((L, d), dtype=f32, **kw)
+        self.token_order = torch.empty((L,), dtype=i32, **kw) if token_order else None
         sizes = [omni_workspace_bytes(OMNI_OP_ROUTER, L, d, Nr, Nc, K, self.N, B, dt),
                  omni_workspace_bytes(OMNI_OP_SCHEDULE, L, d, Nr, Nc, K, self.N, B, dt),
                  omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, Nr, Nc, K, self.N, B, dt)]
@@ -336,10 +356,12 @@ class RoutedBranch:
         return omni_router(x, Wr, Wc, self.K, self.idx, self.score, self.gate, self.ws, stream)
 
     def schedule(self, stream=None):
-        return omni_schedule(self.idx, self.N, self.B, self.perm, self.group_off, self.ws, stream)
+        return omni_schedule(self.idx, self.N, self.B, self.perm, self.group_off, self.ws, stream,
+                             self.token_order)
 
     def expert_forward(self, x, W, V, stream=None):
-        return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.y, self.ws, stream)
+        return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.y, self.ws, stream,
+                                   self.token_order)
 
     def forward(self, x, Wr, Wc, W, V, stream=None):
         self.router(x, Wr, Wc, stream)

@@ -66,6 +66,8 @@ def parse():
                          "(both rates are always given)")
     ap.add_argument("--no-dense-router", action="store_true",
                     help="skip timing the fully connected router of the ablation")
+    ap.add_argument("--token-order", action="store_true",
+                    help="time the step with the token-ordered output pass as the headline")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward calls")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -219,6 +221,41 @@ def time_dense_router(inp, w, router_ms, seed, reps=3):
                     "LogSoftmax over N; the pages report 30.6x latency for this substitution"}
 
 
+def time_token_order(inp, w, br, steps, token_order):
+    """The other setting of the output pass's token order, timed on the same
+    inputs: per-stage medians and whether y matches the headline step's bit
+    for bit (it must: each token's sum keeps its k order)."""
+    import torch
+
+    from atomic_expert_routing_amd import omni
+
+    bo = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype,
+                           token_order=token_order)
+    for _ in range(2):
+        bo.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        bo.router(inp["x"], inp["Wr"], inp["Wc"])
+        ev[1].record()
+        bo.schedule()
+        ev[2].record()
+        bo.expert_forward(inp["x"], inp["W"], inp["V"])
+        ev[3].record()
+        evs.append(ev)
+    torch.cuda.synchronize()
+
+    def med(a, b):
+        return round(statistics.median(e[a].elapsed_time(e[b]) for e in evs), 4)
+
+    same = bool(torch.equal(bo.y, br.y))
+    del bo
+    return {"token_order": token_order, "step_events_ms": med(0, 3), "schedule_ms": med(1, 2),
+            "expert_forward_ms": med(2, 3), "y_bitwise_equal": same}
+
+
 def time_backward(inp, w, br, steps, seed):
     """omni_expert_backward + omni_router_backward on the step's routing, for a
     seeded upstream gradient; preallocated outputs and workspaces.  The expert
@@ -312,7 +349,8 @@ def main():
     w = synth.WORKLOADS[args.workload or synth.HEADLINE]
     log(f"[bench] workload {w.name}: generating inputs on the GPU")
     inp = synth.make_inputs(w, seed=args.seed, device="cuda")
-    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype,
+                           token_order=args.token_order)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -397,7 +435,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype if w.dtype == "bf16" else "f32",
         "data": "synthetic: seeded Gaussian x and random-init W, V, W_r, W_c (no trained weights)",
-        "config": {**w.describe(), "parallelism": "single GPU"},
+        "config": {**w.describe(), "parallelism": "single GPU",
+                   "token_ordered_output": bool(args.token_order)},
         "tokens_per_s": round(w.L / (ms_step * 1e-3), 1),
         "timing": "replays of the step captured as a HIP graph" if args.graph
                   else "eager launches",
@@ -454,6 +493,8 @@ def main():
     tc_ms = statistics.median(tc_times)
     out["token_centric_assembly_ms"] = round(tc_ms, 4)
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
+
+    out["other_token_order"] = time_token_order(inp, w, br, args.steps, not args.token_order)
 
     out["shared_mlp"] = time_mlp(inp, w, args.steps, args.seed, step_ev_ms)
     if not args.no_dense_router:

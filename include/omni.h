@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 4
+#define OMNI_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -121,12 +121,21 @@ OMNI_API omni_status omni_router(const void* x, const void* Wr, const void* Wc,
  *                                  tasks whose group is < q, so group q's
  *                                  tasks are perm[group_off[q] .. group_off[q+1])
  *                                  (empty for an inactive group)
+ *   token_order [L]     int32 out, optional (NULL: not computed)
+ *                                  the tokens stably sorted by the group of
+ *                                  their first expert, idx[t*K] / B (ties by
+ *                                  token id).  Not part of the pages' method:
+ *                                  an execution order for omni_expert_forward's
+ *                                  output pass that puts tokens sharing their
+ *                                  leading experts side by side; it never
+ *                                  changes y.
  * Bit-exact and deterministic.  Requires N >= 1, B >= 1, L*K < 2^31,
- * N < 2^31.  Workspace: sort buffers, O(L*K) int32.
+ * N < 2^31 (and L <= 2^31-8 with token_order).  Workspace: sort buffers,
+ * O(L*K) int32.
  */
 OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
                           int64_t N, int64_t B,
-                          int32_t* perm, int32_t* group_off,
+                          int32_t* perm, int32_t* group_off, int32_t* token_order,
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -141,6 +150,13 @@ OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
  *   idx   [L, K]  int32       expert ids (from omni_router)
  *   gate  [L, K]  fp32        gates      (from omni_router)
  *   perm  [L*K]   int32       schedule   (from omni_schedule)
+ *   token_order [L] int32     optional (NULL: tokens by id); the order in which
+ *                             the output pass visits tokens, each of the 8
+ *                             XCDs taking a contiguous eighth (from
+ *                             omni_schedule's token_order).  Must be a
+ *                             permutation of [0, L): entries outside [0, L)
+ *                             are skipped and a token that never appears keeps
+ *                             its old y row.  y itself does not depend on it.
  *   y     [L, d]  fp32 out    y_t = sum_k gate[t,k] * SiLU(x_t . W[idx[t,k]]) * V[idx[t,k]]
  *                             fully overwritten (no accumulation into old y)
  * SiLU(h) = h / (1 + exp(-h)).  The activation pass walks the tasks in
@@ -152,7 +168,7 @@ OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
  */
 OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const void* V,
                                 const int32_t* idx, const float* gate,
-                                const int32_t* perm,
+                                const int32_t* perm, const int32_t* token_order,
                                 int64_t L, int64_t d, int64_t N, int64_t K,
                                 omni_dtype dt, float* y,
                                 void* ws, size_t ws_bytes, void* stream);

@@ -210,6 +210,18 @@ def schedule(idx, N, B):
     return perm.astype(np.int64), group_off
 
 
+def token_order(idx, B):
+    """Tokens sorted by the group of their first (highest-scoring) expert,
+    ties by token id: tokens whose leading experts share a group come
+    together.  A processing order for the per-token output sum (it changes
+    which tokens run side by side, never a token's result).
+    Returns order [L] int64.
+    """
+    idx = np.asarray(idx, np.int64)
+    L = idx.shape[0]
+    return np.lexsort((np.arange(L), idx[:, 0] // B)).astype(np.int64)
+
+
 # ---------------------------------------------------------------------------
 # Dynamic Expert Assembly  [digest, steps 1 and 3; resume-de 2.1]
 # ---------------------------------------------------------------------------

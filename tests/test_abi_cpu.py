@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 4
+    assert lib.omni_abi_version() == 5
 
 
 def test_status_strings():
@@ -115,11 +115,12 @@ def test_calls_reject_before_launch():
                         fake, 16, None)
     assert s == omni.OMNI_ERR_WORKSPACE and b"workspace" in lib.omni_last_error()
     # misaligned workspace
-    s = lib.omni_schedule(fake, 4, 2, 10, 2, fake, fake, ctypes.c_void_p(4100), 1 << 20, None)
+    s = lib.omni_schedule(fake, 4, 2, 10, 2, fake, fake, None, ctypes.c_void_p(4100), 1 << 20,
+                          None)
     assert s == omni.OMNI_ERR_INVALID_ARG
     # misaligned x
-    s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, 4, 8, 10,
-                                2, omni.OMNI_BF16, fake, fake, 1 << 20, None)
+    s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, None, 4, 8,
+                                10, 2, omni.OMNI_BF16, fake, fake, 1 << 20, None)
     assert s == omni.OMNI_ERR_INVALID_ARG
     # K larger than the grid
     s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 5, omni.OMNI_F32, fake, fake, fake,

@@ -144,6 +144,40 @@ def test_token_centric_baseline_matches_oracle(case):
     check_y(y_tc, to_np(br.y), RTOL_FP32_ARITH)
 
 
+def check_token_order(inp, br, w):
+    """The schedule's token order equals the oracle's (bit-exact), and the
+    output pass that follows it reproduces br.y bit for bit: each token's
+    sum is taken in k order whatever order the tokens run in."""
+    perm, off, order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True)
+    y = omni.omni_expert_forward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, perm,
+                                 token_order=order)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(order), O.token_order(to_np(br.idx), w.B))
+    assert torch.equal(perm, br.perm) and torch.equal(off, br.group_off)
+    assert torch.equal(y, br.y)
+
+
+@pytest.mark.parametrize("case", [RAGGED[0], RAGGED[1], RAGGED[3], RAGGED[6], RAGGED[7],
+                                  RAGGED[9], (1001, 64, 40, 40, 8, 2, "bf16")],
+                         ids=lambda c: "L{}_d{}_{}x{}_K{}_B{}_{}".format(*c))
+def test_token_ordered_output_pass(case):
+    # L from 1 to 1001 (not a multiple of 8: slots past L in the last XCD's
+    # eighth), B = 1 and B > N
+    L, d, Nr, Nc, K, B, dt = case
+    w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, B, dt, seed=zlib.crc32(repr(case).encode()) % 1000)
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    say(f"token order {w.name}")
+    br = run_branch(inp, w)
+    check_token_order(inp, br, w)
+    # through RoutedBranch, run twice (the second over a stale y)
+    bo = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True)
+    for _ in range(2):
+        bo.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+        torch.cuda.synchronize()
+        assert torch.equal(bo.y, br.y)
+        bo.y.fill_(7.0)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = synth.WORKLOADS[synth.TINY]
     inp = {k: v.cuda() for k, v in synth.make_inputs(w, seed=5).items()}
@@ -200,5 +234,8 @@ def test_full_size_workload_sampled(name):
     torch.cuda.synchronize()
     dy = (y_tc - br.y).norm() / br.y.norm()
     assert dy.item() <= RTOL_FP32_ARITH, dy.item()
+    # token-ordered output pass: the order bit-exact, y bitwise unchanged
+    say(f"full-size {name}: token order")
+    check_token_order(inp, br, w)
     del inp, br
     torch.cuda.empty_cache()

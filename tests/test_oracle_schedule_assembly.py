@@ -188,3 +188,13 @@ def test_tiny_workload_end_to_end_consistency():
     y_tc = O.assemble_token_centric(inp["x"], inp["W"], inp["V"], out["idx"], out["gate"])
     np.testing.assert_allclose(out["y"], y_tc, atol=1e-12)
     assert np.abs(out["y"]).max() > 1e-3  # non-degenerate
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(1, 30), st.integers(1, 5), st.integers(6, 60), st.integers(1, 20), st.integers(0, 2**31))
+def test_token_order_matches_python_sorted(L, K, N, B, seed):
+    K = min(K, N)
+    idx = random_idx(rng(seed), L, K, N)
+    order = O.token_order(idx, B)
+    assert order.tolist() == sorted(range(L), key=lambda t: (int(idx[t, 0]) // B, t))
+    assert sorted(order.tolist()) == list(range(L))
