@@ -136,6 +136,20 @@ omni_status dense_router_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dty
   return OMNI_OK;
 }
 
+omni_status blocked_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
+  if (dt != OMNI_BF16)
+    return fail(OMNI_ERR_UNSUPPORTED, "the blocked assembly takes bf16 inputs only (MFMA products)");
+  if (d % omni::BLK_D_TILE)
+    return fail(OMNI_ERR_UNSUPPORTED, "the blocked assembly needs d %% %d == 0 (d=%lld)",
+                omni::BLK_D_TILE, (long long)d);
+  if (L > I32_LIMIT - omni::BLK_TOKENS)
+    return fail(OMNI_ERR_UNSUPPORTED, "L = %lld too large for the blocked assembly", (long long)L);
+  *out = omni::plan_blocked(L, K, N).ws_bytes;
+  return OMNI_OK;
+}
+
 omni_status check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
     return fail(OMNI_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
@@ -208,6 +222,26 @@ omni_status omni_expert_forward(const void* x, const void* W, const void* V, con
   if (e != hipSuccess) return hip_status(e, "expert activation launch");
   e = omni::launch_expert_out(V, idx, act, token_order, (int)L, (int)d, (int)K, dt, y, st);
   return hip_status(e, "expert output launch");
+}
+
+omni_status omni_expert_forward_blocked(const void* x, const void* W, const void* V,
+                                        const int32_t* idx, const float* gate,
+                                        const int32_t* token_order, int64_t L, int64_t d,
+                                        int64_t N, int64_t K, omni_dtype dt, float* y, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = blocked_ws(L, d, N, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !token_order || !y)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward_blocked: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(y))
+    return fail(OMNI_ERR_INVALID_ARG,
+                "omni_expert_forward_blocked: x, W, V and y must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::BlockedPlan plan = omni::plan_blocked(L, K, N);
+  hipError_t e = omni::launch_expert_blocked(x, W, V, idx, gate, token_order, (int)L, (int)d,
+                                             (int)K, y, plan, ws, (hipStream_t)stream);
+  return hip_status(e, "blocked assembly launch");
 }
 
 omni_status omni_expert_forward_token_centric(const void* x, const void* W, const void* V,
@@ -318,6 +352,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_ROUTER_BACKWARD: s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need); break;
     case OMNI_OP_SHARED_MLP: s = mlp_ws(L, d, N, dt, &need); break;
     case OMNI_OP_DENSE_ROUTER: s = dense_router_ws(L, d, N, K, dt, &need); break;
+    case OMNI_OP_EXPERT_FORWARD_BLOCKED: s = blocked_ws(L, d, N, K, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

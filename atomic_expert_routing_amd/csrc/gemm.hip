@@ -5,12 +5,11 @@
 // products, and the shared dense MLP's gate/up and down projections
 // (digest, step 1: the + MLP(x) branch).
 
-#include "omni_internal.h"
+#include "mfma_pipe.h"
 
 namespace omni {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int GEMM_PLAIN = 0, GEMM_SWIGLU = 1;
 
 // ------------------------------------------------------------------ bf16 GEMM, pipelined
@@ -23,45 +22,6 @@ constexpr int GEMM_PLAIN = 0, GEMM_SWIGLU = 1;
 // rows read by one ds_read_b128 over 16 distinct bank groups.  Rows past L
 // or N_r+N_c are loaded from a clamped row (their results are never
 // stored).  Needs d % BK == 0 (no partial k-tile).
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most n loads of this wave are outstanding (n a multiple of
-// the loads per k-tile: 4 or 8).
-template <int N>
-__device__ __forceinline__ void wait_vm_imm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most i * N of this wave's vector loads are outstanding
-// (i = 0 .. MAXI, the k-tiles allowed to stay in flight; N loads per k-tile).
-template <int N, int MAXI>
-__device__ __forceinline__ void wait_vm_tiles(int i) {
-  if constexpr (MAXI >= 3) {
-    if (i >= 3) return wait_vm_imm<3 * N>();
-  }
-  if constexpr (MAXI >= 2) {
-    if (i >= 2) return wait_vm_imm<2 * N>();
-  }
-  if constexpr (MAXI >= 1) {
-    if (i >= 1) return wait_vm_imm<N>();
-  }
-  wait_vm_imm<0>();
-}
-
-// Workgroup barrier without the fence of __syncthreads (which would also
-// wait for every direct-to-LDS load still in flight).
-__device__ __forceinline__ void block_sync_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int BK>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (BK == 64) return (r >> 1) & 7;  // 8 chunks per 128-byte row
-  else return (r >> 2) & 3;                     // 4 chunks per 64-byte row
-}
 
 // MODE GEMM_PLAIN writes fp32 C.  MODE GEMM_SWIGLU is the first half of a
 // SwiGLU block: the B rows are taken as alternating 16-row blocks of B0

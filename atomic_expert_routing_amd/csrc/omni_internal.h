@@ -180,6 +180,21 @@ hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act
                              const int32_t* order, int L, int d, int K, omni_dtype dt, float* y,
                              hipStream_t s);
 
+// ----------------------------------------------------------------- blocked assembly
+constexpr int BLK_TOKENS = 64;       // tokens per block (consecutive entries of the order)
+constexpr int BLK_UNION_TILE = 128;  // union columns per tile
+constexpr int BLK_D_TILE = 256;      // y columns per output tile (d must be a multiple)
+struct BlockedPlan {
+  int nb, ucap, sort_keys;  // blocks, union capacity per block, LDS sort size
+  size_t off_U, off_nU, off_col, off_toff, off_G, off_Ahi, off_Alo, ws_bytes;
+};
+BlockedPlan plan_blocked(int64_t L, int64_t K, int64_t N);
+// y[t] for every t of `order` (a permutation of [0, L)), by dense products over
+// each block of 64 consecutive order entries and the union of their experts
+hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, const int32_t* idx,
+                                 const float* gate, const int32_t* order, int L, int d, int K,
+                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s);
+
 // ----------------------------------------------------------------- dense router
 constexpr int DENSE_ROUTER_CHUNK = 65536;  // experts per logits chunk
 struct DenseRouterPlan {

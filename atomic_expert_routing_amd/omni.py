@@ -16,14 +16,14 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 5
+_ABI_VERSION = 6
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
-OMNI_OP_DENSE_ROUTER = 6
-EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward",
+OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED = 6, 7
+EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
             "omni_shared_mlp", "omni_dense_router", "omni_workspace_bytes", "omni_status_string",
             "omni_last_error", "omni_abi_version")
@@ -54,6 +54,8 @@ def library() -> ctypes.CDLL:
     lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         ctypes.c_int, vp, vp, sz, vp]
+    lib.omni_expert_forward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                       ctypes.c_int, vp, vp]
     lib.omni_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -67,7 +69,7 @@ def library() -> ctypes.CDLL:
                                       sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
-    for f in ("omni_router", "omni_schedule", "omni_expert_forward",
+    for f in ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
               "omni_expert_forward_token_centric", "omni_expert_backward",
               "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
               "omni_workspace_bytes"):
@@ -210,6 +212,30 @@ def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None,
     return y
 
 
+def omni_expert_forward_blocked(x, W, V, idx, gate, token_order, y=None, ws=None, stream=None):
+    """The assembly as dense products over blocks of 64 tokens of token_order
+    and the union of their experts -> y [L, d] float32 (bf16 inputs)."""
+    L, d = x.shape
+    N = W.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    px = _dev(x, "x")
+    pW = _dev(W, "W", x.dtype, (N, d))
+    pV = _dev(V, "V", x.dtype, (N, d))
+    pi = _dev(idx, "idx", torch.int32, (L, K))
+    pg = _dev(gate, "gate", torch.float32, (L, K))
+    pt = _dev(token_order, "token_order", torch.int32, (L,))
+    y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
+    py = _dev(y, "y", torch.float32, (L, d))
+    need = (omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD_BLOCKED, L, d, 1, 1, K, N, 1, dt)
+            if ws is None else 0)
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_expert_forward_blocked(px, pW, pV, pi, pg, pt, L, d, N, K, dt, py, pw,
+                                                 nw, _stream(stream)),
+           "omni_expert_forward_blocked")
+    return y
+
+
 def omni_expert_forward_token_centric(x, W, V, idx, gate, y=None, stream=None):
     """Token-centric baseline of the assembly (no schedule) -> y [L, d] float32."""
     L, d = x.shape
@@ -328,11 +354,14 @@ class RoutedBranch:
     token_order=True the schedule also sorts the tokens by their first
     expert's group and the output pass follows that order: it pays where
     tokens pile onto few experts (clustered routing) and costs a little on
-    spread-out routing.
+    spread-out routing.  assembly="blocked" replaces the per-task assembly by
+    omni_expert_forward_blocked over that order (dense MFMA products per block
+    of 64 tokens and their experts' union): the choice for clustered routing,
+    far slower than the per-task passes on spread-out routing.
     """
 
     def __init__(self, L, d, Nr, Nc, K, B, dtype=torch.bfloat16, device="cuda",
-                 token_order=False):
+                 token_order=False, assembly="expert_centric"):
         self.L, self.d, self.Nr, self.Nc, self.K, self.B = L, d, Nr, Nc, K, B
         self.N = Nr * Nc
         self.G = -(-self.N // B)
@@ -345,10 +374,15 @@ class RoutedBranch:
         self.perm = torch.empty((L * K,), dtype=i32, **kw)
         self.group_off = torch.empty((self.G + 1,), dtype=i32, **kw)
         self.y = torch.empty((L, d), dtype=f32, **kw)
+        if assembly not in ("expert_centric", "blocked"):
+            raise ValueError(f"unknown assembly {assembly!r}")
+        self.assembly = assembly
+        token_order = token_order or assembly == "blocked"  # blocks follow the order
         self.token_order = torch.empty((L,), dtype=i32, **kw) if token_order else None
+        op = OMNI_OP_EXPERT_FORWARD_BLOCKED if assembly == "blocked" else OMNI_OP_EXPERT_FORWARD
         sizes = [omni_workspace_bytes(OMNI_OP_ROUTER, L, d, Nr, Nc, K, self.N, B, dt),
                  omni_workspace_bytes(OMNI_OP_SCHEDULE, L, d, Nr, Nc, K, self.N, B, dt),
-                 omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, Nr, Nc, K, self.N, B, dt)]
+                 omni_workspace_bytes(op, L, d, Nr, Nc, K, self.N, B, dt)]
         # the three calls run in order on one stream, so they share one workspace
         self.ws = torch.empty(max(sizes), dtype=torch.uint8, **kw)
 
@@ -360,6 +394,9 @@ class RoutedBranch:
                              self.token_order)
 
     def expert_forward(self, x, W, V, stream=None):
+        if self.assembly == "blocked":
+            return omni_expert_forward_blocked(x, W, V, self.idx, self.gate, self.token_order,
+                                               self.y, self.ws, stream)
         return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.y, self.ws, stream,
                                    self.token_order)
 

@@ -68,6 +68,9 @@ def parse():
                     help="skip timing the fully connected router of the ablation")
     ap.add_argument("--token-order", action="store_true",
                     help="time the step with the token-ordered output pass as the headline")
+    ap.add_argument("--assembly", choices=("expert_centric", "blocked"), default="expert_centric",
+                    help="assembly of the headline step (blocked: dense products per token "
+                         "block, for clustered routing)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward calls")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -221,16 +224,38 @@ def time_dense_router(inp, w, router_ms, seed, reps=3):
                     "LogSoftmax over N; the pages report 30.6x latency for this substitution"}
 
 
-def time_token_order(inp, w, br, steps, token_order):
-    """The other setting of the output pass's token order, timed on the same
-    inputs: per-stage medians and whether y matches the headline step's bit
-    for bit (it must: each token's sum keeps its k order)."""
+def blocked_roofline(br, w, mean_ms):
+    """The blocked assembly's MFMA work: per block of 64 tokens, 64 x npad x d
+    products on the W side and twice that on the V side (hi and lo terms),
+    npad = the block's union size rounded up to whole 128-column tiles."""
+    import torch
+
+    order = br.token_order.long()
+    npad = 0
+    for b0 in range(0, w.L, 64):
+        u = int(torch.unique(br.idx[order[b0:b0 + 64]]).numel())
+        npad += max(1, -(-u // 128)) * 128
+    flops = 64 * npad * w.d * 2 * 3
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {"kernel": "omni_expert_forward_blocked (blk_union, blk_plan, blk_gates, blk_act, "
+                      "blk_out)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "mfma_flops": flops, "definition_flops": 4 * w.M * w.d,
+            "mean_ms": round(mean_ms, 4)}
+
+
+def time_variant(inp, w, br, steps, token_order, assembly="expert_centric"):
+    """Another configuration of the step timed on the same inputs: per-stage
+    medians, and how its y compares with the headline step's (bitwise for
+    the token order alone, whose sums keep their k order; to fp32 rounding
+    for the blocked assembly)."""
     import torch
 
     from atomic_expert_routing_amd import omni
 
     bo = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype,
-                           token_order=token_order)
+                           token_order=token_order, assembly=assembly)
     for _ in range(2):
         bo.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     torch.cuda.synchronize()
@@ -251,9 +276,11 @@ def time_token_order(inp, w, br, steps, token_order):
         return round(statistics.median(e[a].elapsed_time(e[b]) for e in evs), 4)
 
     same = bool(torch.equal(bo.y, br.y))
+    rel = ((bo.y - br.y).norm() / br.y.norm()).item()
     del bo
-    return {"token_order": token_order, "step_events_ms": med(0, 3), "schedule_ms": med(1, 2),
-            "expert_forward_ms": med(2, 3), "y_bitwise_equal": same}
+    return {"token_order": bool(token_order or assembly == "blocked"), "assembly": assembly,
+            "step_events_ms": med(0, 3), "schedule_ms": med(1, 2), "expert_forward_ms": med(2, 3),
+            "y_bitwise_equal": same, "y_rel_diff": rel}
 
 
 def time_backward(inp, w, br, steps, seed):
@@ -350,7 +377,7 @@ def main():
     log(f"[bench] workload {w.name}: generating inputs on the GPU")
     inp = synth.make_inputs(w, seed=args.seed, device="cuda")
     br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype,
-                           token_order=args.token_order)
+                           token_order=args.token_order, assembly=args.assembly)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -436,7 +463,8 @@ def main():
         "dtype": w.dtype if w.dtype == "bf16" else "f32",
         "data": "synthetic: seeded Gaussian x and random-init W, V, W_r, W_c (no trained weights)",
         "config": {**w.describe(), "parallelism": "single GPU",
-                   "token_ordered_output": bool(args.token_order)},
+                   "token_ordered_output": bool(args.token_order or args.assembly == "blocked"),
+                   "assembly": args.assembly},
         "tokens_per_s": round(w.L / (ms_step * 1e-3), 1),
         "timing": "replays of the step captured as a HIP graph" if args.graph
                   else "eager launches",
@@ -457,7 +485,7 @@ def main():
             "traffic": measured_traffic(w.name),
             "algorithmic_bytes": expert_bytes,
             "mean_ms": round(expert_mean_ms, 4),
-        },
+        } if args.assembly == "expert_centric" else blocked_roofline(br, w, expert_mean_ms),
         "router_gemm_flops": router_flops,
     }
     # cold cache: before each of these steps a 512 MiB fill evicts the 256 MB
@@ -494,7 +522,13 @@ def main():
     out["token_centric_assembly_ms"] = round(tc_ms, 4)
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
 
-    out["other_token_order"] = time_token_order(inp, w, br, args.steps, not args.token_order)
+    variants = []
+    if args.assembly == "expert_centric":
+        variants.append(time_variant(inp, w, br, args.steps, not args.token_order))
+    if w.dtype == "bf16" and w.d % 256 == 0:
+        variants.append(time_variant(inp, w, br, args.steps, True,
+                                     "expert_centric" if args.assembly == "blocked" else "blocked"))
+    out["variants"] = variants
 
     out["shared_mlp"] = time_mlp(inp, w, args.steps, args.seed, step_ev_ms)
     if not args.no_dense_router:

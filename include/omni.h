@@ -7,7 +7,9 @@
  *   omni_router          Cartesian Product Router: ids, scores, gates
  *   omni_schedule        expert-centric schedule: sorted tasks, group offsets
  *   omni_expert_forward  Dynamic Expert Assembly: y
- * and one comparison baseline, omni_expert_forward_token_centric.
+ * with a dense variant of the assembly for routing in which many tokens share
+ * experts, omni_expert_forward_blocked, and one comparison baseline,
+ * omni_expert_forward_token_centric.
  * The backward of the branch runs in two more calls:
  *   omni_expert_backward  dx (expert part), d gate, dW and dV of used experts
  *   omni_router_backward  dW_r, dW_c, and the router part added into dx
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 5
+#define OMNI_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -70,7 +72,8 @@ typedef enum {
   OMNI_OP_EXPERT_BACKWARD = 3,
   OMNI_OP_ROUTER_BACKWARD = 4,
   OMNI_OP_SHARED_MLP = 5, /* omni_workspace_bytes takes d_ff in its N argument */
-  OMNI_OP_DENSE_ROUTER = 6
+  OMNI_OP_DENSE_ROUTER = 6,
+  OMNI_OP_EXPERT_FORWARD_BLOCKED = 7
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -172,6 +175,42 @@ OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const voi
                                 int64_t L, int64_t d, int64_t N, int64_t K,
                                 omni_dtype dt, float* y,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_expert_forward_blocked - the same y as omni_expert_forward, as dense
+ * MFMA products over blocks of tokens, for routing in which many tokens share
+ * their experts.
+ * Source: the assembly O_q = (G_q . sigma(X_q W_q^T)) V_q of the OmniMoE
+ * digest, method paragraph, step 3 (gist.science resume section 2.1), with
+ * the group formed the other way round: the tokens are cut into blocks of
+ * 64 consecutive entries of token_order, and block b's group is the union
+ * U_b of its tokens' experts.  Each block computes
+ *   A_b = G_b . SiLU(X_b W[U_b]^T)  (G_b: the gates, zero off the tasks)
+ *   y_b = A_b V[U_b]
+ * so each weight row of the union is read once per block and serves all of
+ * the block's tokens.  The W-side product is exact in bf16 x bf16 with fp32
+ * accumulation; A enters the V-side product as two bf16 terms (hi + lo,
+ * about 16 significant bits); sums are fp32, in an order that differs from
+ * omni_expert_forward's, so y agrees with it to fp32 rounding, not bitwise
+ * (deterministic run to run).
+ *
+ *   x, W, V, idx, gate, y   as for omni_expert_forward
+ *   token_order [L] int32   a permutation of [0, L) (omni_schedule's
+ *                           token_order groups tokens that share experts;
+ *                           any permutation gives the same y, at a cost that
+ *                           grows with the blocks' union sizes)
+ * Requires bf16, d % 256 == 0, K <= OMNI_MAX_K, the K ids of each token
+ * distinct (as omni_router returns them), L*K < 2^31, N < 2^31.  Entries of
+ * token_order outside [0, L) are skipped (their y rows are not written).
+ * Workspace (omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD_BLOCKED)): the
+ * unions, the gate and activation tiles at the largest union each block can
+ * have (64 * min(64 K, N) entries per block); roughly 8 B * 64 * L * K.
+ */
+OMNI_API omni_status omni_expert_forward_blocked(const void* x, const void* W, const void* V,
+                                                 const int32_t* idx, const float* gate,
+                                                 const int32_t* token_order, int64_t L, int64_t d,
+                                                 int64_t N, int64_t K, omni_dtype dt, float* y,
+                                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * omni_expert_forward_token_centric - the same y as omni_expert_forward,

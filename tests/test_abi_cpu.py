@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 5
+    assert lib.omni_abi_version() == 6
 
 
 def test_status_strings():
@@ -99,7 +99,7 @@ def test_schedule_validation():
         with pytest.raises(omni.OmniError):
             omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, **args)
     with pytest.raises(omni.OmniError):
-        omni.omni_workspace_bytes(7)
+        omni.omni_workspace_bytes(8)
 
 
 def test_calls_reject_before_launch():
@@ -191,6 +191,39 @@ def test_dense_router_workspace_and_validation():
         assert e.value.status == st
     assert omni.omni_workspace_bytes(omni.OMNI_OP_DENSE_ROUTER, L=8, d=72, K=4, N=100,
                                      dtype=omni.OMNI_F32) > 0
+
+
+def test_blocked_workspace_and_validation():
+    """Blocks of 64 tokens; each block's union holds at most min(64 K, N) ids,
+    padded to 128-column tiles; gate (fp32) and activation (2 x bf16) tiles
+    are sized for every block at its largest union."""
+    def a256(n):
+        return (n + 255) // 256 * 256
+
+    for L, K, N in ((16384, 256, 1700416), (4096, 128, 1700416), (100, 16, 1024), (65, 8, 50)):
+        nb = -(-L // 64)
+        nt = 64 * K
+        ucap = -(-min(nt, N) // 128) * 128
+        elems = nb * 64 * ucap
+        want = (a256(nb * ucap * 4) + a256(nb * 4) + a256(nb * nt * 4) + a256((nb + 1) * 4)
+                + a256(elems * 4) + 2 * a256(elems * 2))
+        got = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, L=L, d=2048, K=K, N=N)
+        assert got == want, (L, K, N)
+    for kw, st in ((dict(dtype=omni.OMNI_F32), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(d=320), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(K=513), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(N=0), omni.OMNI_ERR_INVALID_ARG)):
+        args = dict(L=128, d=256, K=16, N=1000)
+        args.update(kw)
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, **args)
+        assert e.value.status == st
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)
+    # the token order is required
+    s = lib.omni_expert_forward_blocked(fake, fake, fake, fake, fake, None, 64, 256, 1000, 8,
+                                        omni.OMNI_BF16, fake, fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
 
 
 def test_binding_rejects_cpu_tensors():
