@@ -186,7 +186,7 @@ constexpr int BLK_UNION_TILE = 128;  // union columns per tile
 constexpr int BLK_D_TILE = 256;      // y columns per output tile (d must be a multiple)
 struct BlockedPlan {
   int nb, ucap, sort_keys;  // blocks, union capacity per block, LDS sort size
-  size_t off_U, off_nU, off_col, off_toff, off_G, off_Ahi, off_Alo, ws_bytes;
+  size_t off_U, off_nU, off_toff, off_G, off_Ahi, off_Alo, ws_bytes;
 };
 BlockedPlan plan_blocked(int64_t L, int64_t K, int64_t N);
 // y[t] for every t of `order` (a permutation of [0, L)), by dense products over

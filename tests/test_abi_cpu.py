@@ -202,10 +202,9 @@ def test_blocked_workspace_and_validation():
 
     for L, K, N in ((16384, 256, 1700416), (4096, 128, 1700416), (100, 16, 1024), (65, 8, 50)):
         nb = -(-L // 64)
-        nt = 64 * K
-        ucap = -(-min(nt, N) // 128) * 128
+        ucap = -(-min(64 * K, N) // 128) * 128
         elems = nb * 64 * ucap
-        want = (a256(nb * ucap * 4) + a256(nb * 4) + a256(nb * nt * 4) + a256((nb + 1) * 4)
+        want = (a256(nb * ucap * 4) + a256(nb * 4) + a256((nb + 1) * 4)
                 + a256(elems * 4) + 2 * a256(elems * 2))
         got = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, L=L, d=2048, K=K, N=N)
         assert got == want, (L, K, N)
