@@ -485,21 +485,45 @@ hipError_t launch_expert_backward(const void* x, const void* W, const void* V, c
   char* w = (char*)ws;
   float* dh = (float*)(w + p.off_dh);
   float* ga = (float*)(w + p.off_ga);
+  const bool bf = dt == OMNI_BF16;
+  hipError_t e = bf ? launch_bwd_token_t<true>(x, W, V, idx, gate, dy, L, d, K, dx, dgate, dh, ga, s)
+                    : launch_bwd_token_t<false>(x, W, V, idx, gate, dy, L, d, K, dx, dgate, dh, ga, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_grad_rows(x, dy, idx, L, d, N, K, dt, uniq, n_uniq, grad_dt, dW_rows, dV_rows,
+                                 p, ws, s);
+}
+
+hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int32_t* n_uniq,
+                                  const BwdPlan& p, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
   int32_t* perm = (int32_t*)(w + p.off_perm);
   int32_t* eoff = (int32_t*)(w + p.off_eoff);
   int32_t* seg = (int32_t*)(w + p.off_seg);
   int* cnt = (int*)(w + p.off_cnt);
   void* sws = w + p.off_sched;
-  const bool bf = dt == OMNI_BF16;
-  hipError_t e = bf ? launch_bwd_token_t<true>(x, W, V, idx, gate, dy, L, d, K, dx, dgate, dh, ga, s)
-                    : launch_bwd_token_t<false>(x, W, V, idx, gate, dy, L, d, K, dx, dgate, dh, ga, s);
-  if (e != hipSuccess) return e;
   // tasks sorted by expert id: the schedule with groups of one expert
-  if ((e = launch_schedule(idx, p.M, 1, N, p.sched, perm, eoff, sws, s)) != hipSuccess) return e;
+  hipError_t e = launch_schedule(idx, p.M, 1, N, p.sched, perm, eoff, sws, s);
+  if (e != hipSuccess) return e;
   const int32_t* keys = schedule_sorted_keys(p.sched, sws);
   hipLaunchKernelGGL(seg_count, dim3(p.ntiles), dim3(SEG_THREADS), 0, s, keys, p.M, cnt);
   hipLaunchKernelGGL(seg_scan, dim3(1), dim3(SEG_THREADS), 0, s, cnt, p.ntiles, p.M, n_uniq, seg);
   hipLaunchKernelGGL(seg_write, dim3(p.ntiles), dim3(SEG_THREADS), 0, s, keys, p.M, cnt, uniq, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_grad_rows(const void* x, const float* dy, const int32_t* idx, int L, int d,
+                                   int N, int K, omni_dtype dt, int32_t* uniq, int32_t* n_uniq,
+                                   omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                   const BwdPlan& p, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  float* dh = (float*)(w + p.off_dh);
+  float* ga = (float*)(w + p.off_ga);
+  const int32_t* perm = (const int32_t*)(w + p.off_perm);
+  const int32_t* seg = (const int32_t*)(w + p.off_seg);
+  const bool bf = dt == OMNI_BF16;
+  (void)L;
+  hipError_t e = launch_expert_segments(idx, N, uniq, n_uniq, p, ws, s);
+  if (e != hipSuccess) return e;
   const int E = bf ? 8 : 4;
   const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
   const dim3 grid((unsigned)p.U_max);

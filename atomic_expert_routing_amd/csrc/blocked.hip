@@ -143,7 +143,8 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
                                                   const float* __restrict__ gate,
                                                   const int32_t* __restrict__ order, int L, int K,
                                                   int ucap, int32_t* __restrict__ U,
-                                                  int32_t* __restrict__ nU, float* __restrict__ G) {
+                                                  int32_t* __restrict__ nU, float* __restrict__ G,
+                                                  int32_t* __restrict__ kmap) {
   extern __shared__ int keys[];
   __shared__ int wtot[16];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -236,7 +237,9 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
     for (int q = 0; q < E; ++q) {
       if (id0[q] == INT_MAX) continue;  // padding or an empty row
       const int c = base[q] + (keys[base[q]] < id0[q]);
-      Gb[((tid * E + q) / K) * npad + c] = __float_as_uint(g0[q]);
+      const int i = tid * E + q, r = i / K;
+      Gb[r * npad + c] = __float_as_uint(g0[q]);
+      if (kmap) kmap[(size_t)b * BT * ucap + r * npad + c] = i - r * K;
     }
   } else {
     for (int i = tid; i < nt; i += 1024) {
@@ -244,7 +247,9 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
       const int t = slot_token(order, b * BT + r, L);
       if (t < 0) continue;
       const size_t m = (size_t)t * K + (i - r * K);
-      Gb[r * npad + position(idx[m])] = __float_as_uint(gate[m]);
+      const int c = position(idx[m]);
+      Gb[r * npad + c] = __float_as_uint(gate[m]);
+      if (kmap) kmap[(size_t)b * BT * ucap + r * npad + c] = i - r * K;
     }
   }
 }
@@ -308,15 +313,36 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+__device__ __forceinline__ float sigmoid(float h) { return 1.f / (1.f + expf(-h)); }
+
+// MODE BLK_FWD: one product, H = X_b W[U_b]^T; the epilogue writes
+// A = G . SiLU(H) as hi + lo bf16 tiles.
+// MODE BLK_BWD: three products through the same pipeline, H = X_b W[U_b]^T
+// and D = dy_b V[U_b]^T with dy_b = dy_hi + dy_lo (two bf16 terms); at each
+// task (t, k) the epilogue writes, with g its gate, s = SiLU(h) and
+// s' = sig(h) (1 + h (1 - sig(h))):
+//   dgate[t,k] = D s,   dh[t,k] = g D s',   ga[t,k] = g s
+// and the dense tile dH = (task ? g D s' : 0) as hi + lo bf16 (for dx = dH W).
+constexpr int BLK_FWD = 0, BLK_BWD = 1;
+
+template <int MODE>
 __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
                                                const uint16_t* __restrict__ W,
+                                               const uint16_t* __restrict__ dyh,
+                                               const uint16_t* __restrict__ dyl,
+                                               const uint16_t* __restrict__ V,
                                                const int32_t* __restrict__ order,
                                                const int32_t* __restrict__ U,
                                                const int32_t* __restrict__ toff,
-                                               const float* __restrict__ G, int L, int d, int nb,
-                                               int ucap, uint16_t* __restrict__ Ahi,
-                                               uint16_t* __restrict__ Alo) {
+                                               const float* __restrict__ G,
+                                               const int32_t* __restrict__ kmap, int L, int d,
+                                               int K, int nb, int ucap,
+                                               uint16_t* __restrict__ Ahi,
+                                               uint16_t* __restrict__ Alo,
+                                               float* __restrict__ dgate, float* __restrict__ dh,
+                                               float* __restrict__ ga) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm1[];
+  constexpr int PHASES = MODE == BLK_FWD ? 1 : 3;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = toff[nb];
@@ -331,35 +357,38 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
     const int j = T - toff[b];
     const int npad = (toff[b + 1] - toff[b]) * UPAD;
     const int32_t* Ub = U + (size_t)b * ucap + j * UPAD;
-    const uint16_t* asrc[K1_LPWA];
-    const uint16_t* bsrc[K1_LPWB];
+    size_t aro[K1_LPWA], bro[K1_LPWB];  // element offsets of this lane's 16-byte chunks
 #pragma unroll
     for (int q = 0; q < K1_LPWA; ++q) {
       const int r = (wave * K1_LPWA + q) * K1_RPI + lane / K1_CPR;
       const int chunk = (lane % K1_CPR) ^ chunk_swz<K1_BK>(r);
       const int t = slot_token(order, b * BT + r, L);
-      asrc[q] = x + (size_t)(t < 0 ? 0 : t) * d + chunk * 8;  // empty rows: any row, masked
+      aro[q] = (size_t)(t < 0 ? 0 : t) * d + chunk * 8;  // empty rows: any row, masked
     }
 #pragma unroll
     for (int q = 0; q < K1_LPWB; ++q) {
       const int r = (wave * K1_LPWB + q) * K1_RPI + lane / K1_CPR;
       const int chunk = (lane % K1_CPR) ^ chunk_swz<K1_BK>(r);
-      bsrc[q] = W + (size_t)Ub[r] * d + chunk * 8;
+      bro[q] = (size_t)Ub[r] * d + chunk * 8;
     }
-    auto issue = [&](int kt) {
-      unsigned char* st = sm1 + (kt % K1_S) * K1_STAGE;
-      const int k0 = kt * K1_BK;
+    // k-tile kk of the concatenated products: phase kk / nk, depth kk % nk
+    auto issue = [&](int kk) {
+      unsigned char* st = sm1 + (kk % K1_S) * K1_STAGE;
+      const int ph = kk / nk, k0 = (kk - ph * nk) * K1_BK;
+      const uint16_t* A = ph == 0 ? x : (ph == 1 ? dyh : dyl);
+      const uint16_t* B = ph == 0 ? W : V;
 #pragma unroll
       for (int q = 0; q < K1_LPWA; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(asrc[q] + k0),
+        __builtin_amdgcn_global_load_lds((const void*)(A + aro[q] + k0),
                                          (lds_void*)(st + (wave * K1_LPWA + q) * 1024), 16, 0, 0);
 #pragma unroll
       for (int q = 0; q < K1_LPWB; ++q)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(bsrc[q] + k0),
+            (const void*)(B + bro[q] + k0),
             (lds_void*)(st + K1_TILEA + (wave * K1_LPWB + q) * 1024), 16, 0, 0);
     };
-    f32x4 acc[K1_MI][K1_NJ];
+    // acc: H, then (backward) D; hs keeps H once the D phases begin
+    f32x4 acc[K1_MI][K1_NJ], hs[MODE == BLK_BWD ? K1_MI : 1][K1_NJ];
 #pragma unroll
     for (int i = 0; i < K1_MI; ++i)
 #pragma unroll
@@ -378,15 +407,7 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
         bfr[q] = *(const bf16x8*)(st + K1_TILEA + r * K1_ROWB + ((kc ^ chunk_swz<K1_BK>(r)) << 4));
       }
     };
-    for (int kt = 0; kt < K1_S - 1 && kt < nk; ++kt) issue(kt);
-    for (int kt = 0; kt < nk; ++kt) {
-      // tile kt landed for this wave (the loads of at most S-2 later tiles may
-      // still fly); after the barrier it has for every wave, and tile kt-1's
-      // stage is free for tile kt+S-1
-      wait_vm_tiles<K1_LPWA + K1_LPWB, K1_S - 2>(min(K1_S - 2, nk - 1 - kt));
-      block_sync_lds();
-      if (kt + K1_S - 1 < nk) issue(kt + K1_S - 1);
-      const unsigned char* st = sm1 + (kt % K1_S) * K1_STAGE;
+    auto multiply = [&](const unsigned char* st, f32x4 (&c)[K1_MI][K1_NJ]) {
       bf16x8 af[2][K1_MI], bfr[2][K1_NJ];
       load_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
@@ -396,11 +417,33 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
         for (int i = 0; i < K1_MI; ++i)
 #pragma unroll
           for (int q = 0; q < K1_NJ; ++q)
-            acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][q],
-                                                                acc[i][q], 0, 0, 0);
+            c[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][i], bfr[ks & 1][q],
+                                                              c[i][q], 0, 0, 0);
       }
+    };
+    const int nkk = PHASES * nk;
+    for (int kk = 0; kk < K1_S - 1 && kk < nkk; ++kk) issue(kk);
+    for (int kk = 0; kk < nkk; ++kk) {
+      // tile kk landed for this wave (the loads of at most S-2 later tiles may
+      // still fly); after the barrier it has for every wave, and tile kk-1's
+      // stage is free for tile kk+S-1
+      wait_vm_tiles<K1_LPWA + K1_LPWB, K1_S - 2>(min(K1_S - 2, nkk - 1 - kk));
+      block_sync_lds();
+      if (kk + K1_S - 1 < nkk) issue(kk + K1_S - 1);
+      const unsigned char* st = sm1 + (kk % K1_S) * K1_STAGE;
+      if constexpr (MODE == BLK_BWD) {
+        if (kk == nk) {  // H is complete: keep it, accumulate D from zero
+#pragma unroll
+          for (int i = 0; i < K1_MI; ++i)
+#pragma unroll
+            for (int q = 0; q < K1_NJ; ++q) {
+              hs[i][q] = acc[i][q];
+              acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
+      multiply(st, acc);
     }
-    // epilogue: a = g * SiLU(h) where (r, c) is a task, else 0; a = hi + lo
     const size_t go = (size_t)b * BT * ucap;  // block b's G and A tiles
     const uint32_t* Gb = (const uint32_t*)G + go;
 #pragma unroll
@@ -413,8 +456,20 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
           const int c = j * UPAD + wn + q * 16 + (lane & 15);
           const size_t o = (size_t)r * npad + c;
           const uint32_t gb = Gb[o];
-          const float h = acc[i][q][e];
-          const float a = gb == NOTASK ? 0.f : __uint_as_float(gb) * (h / (1.f + expf(-h)));
+          float a = 0.f;
+          if constexpr (MODE == BLK_FWD) {
+            const float h = acc[i][q][e];
+            if (gb != NOTASK) a = __uint_as_float(gb) * (h * sigmoid(h));
+          } else if (gb != NOTASK) {
+            const float h = hs[i][q][e];
+            const float g = __uint_as_float(gb), D = acc[i][q][e], sg = sigmoid(h);
+            const float sl = h * sg, slp = sg * (1.f + h * (1.f - sg));
+            a = g * D * slp;  // dh
+            const size_t m = (size_t)order[b * BT + r] * K + kmap[go + o];
+            dgate[m] = D * sl;
+            dh[m] = a;
+            ga[m] = g * sl;
+          }
           const uint16_t hi = bf16_rne(a);
           Ahi[go + o] = hi;
           Alo[go + o] = bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
@@ -438,116 +493,313 @@ constexpr int K2_VT = K2_KT * K2_ROWB;           // 16 KB V slice
 constexpr int K2_AT = BT * K2_KT * 2;            // 4 KB per A term
 constexpr int K2_STAGE = K2_VT + 2 * K2_AT;      // 24 KB
 constexpr int K2_S = 3;
-constexpr int K2_TILE_OPS = 6;  // vector loads per wave and k-tile: 4 of V, 1 each of A_hi, A_lo
-
+// SETS false: workgroup (b, jt) as above; A and U at fixed per-block offsets
+// (b * 64 * ucap, b * ucap); output row r of block b is token order[64 b + r].
+// SETS true (the expert-set products of the backward): persistent over the
+// items (set b, column tile jt) of the *nrows / 64 sets; A, U and the k-tile
+// count come from the compact tile prefix toff; output row r of set b is row
+// order[64 b + r] of y (an expert's rank among the used experts).
+// NB = 2 takes the B rows as two bf16 terms (hi, lo): the products are
+// A_hi B_hi + A_lo B_hi + A_hi B_lo.  OUT_BF16 writes y rounded to bf16.
+template <bool SETS, int NB, bool OUT_BF16>
 __global__ __launch_bounds__(256) void blk_out(const uint16_t* __restrict__ V,
+                                               const uint16_t* __restrict__ V2,
                                                const int32_t* __restrict__ order,
+                                               const int32_t* __restrict__ nrows,
                                                const int32_t* __restrict__ U,
                                                const int32_t* __restrict__ toff,
                                                const uint16_t* __restrict__ Ahi,
                                                const uint16_t* __restrict__ Alo, int L, int d,
-                                               int ucap, float* __restrict__ y) {
+                                               int ucap, void* __restrict__ y_) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm2[];
+  constexpr int STAGE = NB * K2_VT + 2 * K2_AT;
+  constexpr int OPS = 4 * NB + 2;  // vector loads per wave and k-tile
   const int tiles_y = d / K2_COLS;
-  // workgroup (b, jt) = b * tiles_y + jt runs on XCD (b * tiles_y + jt) % 8:
-  // at d = 2048 each XCD takes one column slice of every block, in block
-  // order, so consecutive blocks of a token cluster share its V slice rows
-  // (measured faster than giving each XCD a contiguous range of blocks,
-  // whose union sizes differ)
-  const int b = blockIdx.x / tiles_y, c0 = (blockIdx.x % tiles_y) * K2_COLS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int npad = (toff[b + 1] - toff[b]) * UPAD;
-  const int nk = npad / K2_KT;
-  const size_t go = (size_t)b * BT * ucap;  // block b's A tiles
-  // V loads: wave w, load q covers LDS rows 8w + 2q and 8w + 2q + 1 (lanes
-  // 0-31 and 32-63), i.e. union rows 8w .. 8w+7 of the tile
-  const int32_t* Uw = U + (size_t)b * ucap + 8 * wave;
-  const int half = lane >> 5;
+  const int half = lane >> 5, kq = lane >> 4;
   int slotg[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) slotg[q] = (lane & 31) ^ (((8 * wave + 2 * q + half) >> 3) & 3);
-  // A loads: wave w covers rows 16w .. 16w+15 of each term (64-byte rows)
-  const size_t aoff = go + (size_t)(16 * wave + (lane >> 2)) * npad + (lane & 3) * 8;
-  const uint16_t* ah_src = Ahi + aoff;
-  const uint16_t* al_src = Alo + aoff;
-  auto load_ids = [&](int kt, int* e) {
+  const int rows = SETS ? *nrows : L;
+  auto item = [&](int b, int c0) {
+    const int ntile = SETS ? toff[b + 1] - toff[b] : 0;
+    const int npad = SETS ? ntile * UPAD : (toff[b + 1] - toff[b]) * UPAD;
+    const int nk = npad / K2_KT;
+    const size_t go = SETS ? (size_t)toff[b] * BT * UPAD : (size_t)b * BT * ucap;
+    // V loads: wave w, load q covers LDS rows 8w + 2q and 8w + 2q + 1 (lanes
+    // 0-31 and 32-63), i.e. union rows 8w .. 8w+7 of the tile
+    const int32_t* Uw = U + (SETS ? (size_t)toff[b] * UPAD : (size_t)b * ucap) + 8 * wave;
+    // A loads: wave w covers rows 16w .. 16w+15 of each term (64-byte rows)
+    const size_t aoff = go + (size_t)(16 * wave + (lane >> 2)) * npad + (lane & 3) * 8;
+    auto load_ids = [&](int kt, int* e) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = Uw[kt * K2_KT + j];
-  };
-  auto issue = [&](int kt, const int* e) {
-    unsigned char* st = sm2 + (kt % K2_S) * K2_STAGE;
+      for (int j = 0; j < 8; ++j) e[j] = Uw[kt * K2_KT + j];
+    };
+    auto issue = [&](int kt, const int* e) {
+      unsigned char* st = sm2 + (kt % K2_S) * STAGE;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int id = half ? e[2 * q + 1] : e[2 * q];
-      __builtin_amdgcn_global_load_lds((const void*)(V + (size_t)id * d + c0 + slotg[q] * 8),
-                                       (lds_void*)(st + (4 * wave + q) * 1024), 16, 0, 0);
-    }
-    __builtin_amdgcn_global_load_lds((const void*)(ah_src + kt * K2_KT),
-                                     (lds_void*)(st + K2_VT + wave * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(al_src + kt * K2_KT),
-                                     (lds_void*)(st + K2_VT + K2_AT + wave * 1024), 16, 0, 0);
-  };
-  f32x4 acc[4][4];
+      for (int q = 0; q < 4; ++q) {
+        const size_t ro = (size_t)(half ? e[2 * q + 1] : e[2 * q]) * d + c0 + slotg[q] * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(V + ro),
+                                         (lds_void*)(st + (4 * wave + q) * 1024), 16, 0, 0);
+        if constexpr (NB == 2)
+          __builtin_amdgcn_global_load_lds((const void*)(V2 + ro),
+                                           (lds_void*)(st + K2_VT + (4 * wave + q) * 1024), 16,
+                                           0, 0);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(Ahi + aoff + kt * K2_KT),
+                                       (lds_void*)(st + NB * K2_VT + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Alo + aoff + kt * K2_KT),
+                                       (lds_void*)(st + NB * K2_VT + K2_AT + wave * 1024), 16, 0,
+                                       0);
+    };
+    f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // ids of even and odd k-tiles, read two tiles before the tile is issued
-  int e0[8], e1[8];
-  load_ids(0, e0);
-  if (nk > 1) load_ids(1, e1);
-  issue(0, e0);
-  if (nk > 1) issue(1, e1);
-  if (nk > 2) load_ids(2, e0);
-  if (nk > 3) load_ids(3, e1);
-  const int kq = lane >> 4;  // k rows 8 kq .. 8 kq + 7 of a fragment
-  auto step = [&](int kt, int* e) {  // e: the id set of tile kt+2 (then of kt+4)
-    // tile kt landed for this wave (only tile kt+1's loads may still fly) ...
-    wait_vm_tiles<K2_TILE_OPS, 1>(kt + 1 < nk);
-    block_sync_lds();  // ... and for every wave; tile kt-1's stage is free
-    if (kt + 2 < nk) {
-      issue(kt + 2, e);
-      if (kt + 4 < nk) load_ids(kt + 4, e);
-    }
-    const unsigned char* st = sm2 + (kt % K2_S) * K2_STAGE;
-    bf16x8 ah[4], al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = (i * 16 + (lane & 15)) * 64 + kq * 16;
-      ah[i] = *(const bf16x8*)(st + K2_VT + o);
-      al[i] = *(const bf16x8*)(st + K2_VT + K2_AT + o);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = wave * 64 + q * 16 + (lane & 15);
-      const unsigned char* p = st + (((col >> 3) ^ kq) << 4) + ((col & 7) << 1);
+      for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ids of even and odd k-tiles, read two tiles before the tile is issued
+    int e0[8], e1[8];
+    if (nk > 0) load_ids(0, e0);
+    if (nk > 1) load_ids(1, e1);
+    if (nk > 0) issue(0, e0);
+    if (nk > 1) issue(1, e1);
+    if (nk > 2) load_ids(2, e0);
+    if (nk > 3) load_ids(3, e1);
+    auto vfrag = [&](const unsigned char* p) {
       bf16x8 vb;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vb[e] = __builtin_bit_cast(__bf16, *(const uint16_t*)(p + (8 * kq + e) * K2_ROWB));
+      return vb;
+    };
+    auto step = [&](int kt, int* e) {  // e: the id set of tile kt+2 (then of kt+4)
+      // tile kt landed for this wave (only tile kt+1's loads may still fly) ...
+      wait_vm_tiles<OPS, 1>(kt + 1 < nk);
+      block_sync_lds();  // ... and for every wave; tile kt-1's stage is free
+      if (kt + 2 < nk) {
+        issue(kt + 2, e);
+        if (kt + 4 < nk) load_ids(kt + 4, e);
+      }
+      const unsigned char* st = sm2 + (kt % K2_S) * STAGE;
+      bf16x8 ah[4], al[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], vb, acc[i][q], 0, 0, 0);
-        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], vb, acc[i][q], 0, 0, 0);
+        const int o = (i * 16 + (lane & 15)) * 64 + kq * 16;
+        ah[i] = *(const bf16x8*)(st + NB * K2_VT + o);
+        al[i] = *(const bf16x8*)(st + NB * K2_VT + K2_AT + o);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wave * 64 + q * 16 + (lane & 15);
+        const unsigned char* p = st + (((col >> 3) ^ kq) << 4) + ((col & 7) << 1);
+        const bf16x8 vb = vfrag(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], vb, acc[i][q], 0, 0, 0);
+          acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], vb, acc[i][q], 0, 0, 0);
+        }
+        if constexpr (NB == 2) {
+          const bf16x8 vl = vfrag(p + K2_VT);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], vl, acc[i][q], 0, 0, 0);
+        }
+      }
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, e0);
+      if (kt + 1 < nk) step(kt + 1, e1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + 4 * (lane >> 4) + e;
+        int t;
+        if constexpr (SETS) t = b * BT + r < rows ? order[b * BT + r] : -1;
+        else t = slot_token(order, b * BT + r, L);
+        if (t < 0) continue;
+        const size_t o = (size_t)t * d + c0 + wave * 64 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (OUT_BF16) ((uint16_t*)y_)[o + q * 16] = bf16_rne(acc[i][q][e]);
+          else ((float*)y_)[o + q * 16] = acc[i][q][e];
+        }
+      }
+  };
+  if constexpr (!SETS) {
+    // workgroup (b, jt) = b * tiles_y + jt runs on XCD (b * tiles_y + jt) % 8:
+    // at d = 2048 each XCD takes one column slice of every block, in block
+    // order, so consecutive blocks of a token cluster share its V slice rows
+    // (measured faster than giving each XCD a contiguous range of blocks,
+    // whose union sizes differ)
+    item(blockIdx.x / tiles_y, (blockIdx.x % tiles_y) * K2_COLS);
+  } else {
+    const int items = (rows + BT - 1) / BT * tiles_y;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+      item(it / tiles_y, (it % tiles_y) * K2_COLS);
+      block_sync_lds();  // every wave is done with the stages before the next item refills them
+    }
+  }
+}
+
+// ------------------------------------------------------------------ expert sets
+// The backward's dW and dV rows as dense products over sets of 64 used
+// experts: the experts are ordered by the first position, in the token order,
+// of a token that uses them (experts of one token cluster come together), set
+// s is experts 64 s .. 64 s + 63 of that order, T_s the union of their
+// tokens (ascending), and with DhT_s [64 x |T_s|] holding dh of each task
+// (zero elsewhere) and GaT_s likewise g SiLU(h):
+//   dW rows of set s = DhT_s X[T_s],   dV rows = GaT_s dy[T_s]
+// (blk_out in its set form).  Each expert belongs to one set, so every row
+// is written once, by the workgroup that sums it.
+
+// pos[order[s]] = s
+__global__ __launch_bounds__(256) void inv_order(const int32_t* __restrict__ order, int L,
+                                                 int32_t* __restrict__ pos) {
+  for (int s = blockIdx.x * 256 + threadIdx.x; s < L; s += gridDim.x * 256) {
+    const int t = order[s];
+    if ((unsigned)t < (unsigned)L) pos[t] = s;
+  }
+}
+
+// key[u] = the smallest pos of a token of used expert u (u < n_uniq), L for
+// the capacity slots past n_uniq; one wave per expert
+__global__ __launch_bounds__(256) void set_keys(const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ seg,
+                                                const int32_t* __restrict__ n_uniq,
+                                                const int32_t* __restrict__ pos, int K, int L,
+                                                int ucap_e, int32_t* __restrict__ key) {
+  const int n = *n_uniq, lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  for (int u = blockIdx.x * 4 + (threadIdx.x >> 6); u < ucap_e; u += nw) {
+    unsigned m = (unsigned)L;
+    if (u < n) {
+      for (int i = seg[u] + lane; i < seg[u + 1]; i += 64)
+        m = min(m, min((unsigned)pos[perm[i] / K], (unsigned)L));
+      m = wave_umin(m);
+    }
+    if (lane == 0) key[u] = (int)m;
+  }
+}
+
+// Per set: the token union by an LDS bitmap over [0, L) and the exclusive
+// prefix of its word popcounts (a token's rank in the union).  COUNT writes
+// the union size; otherwise the union (padded with token 0 up to whole
+// 128-entry tiles) and the dense tiles DhT, GaT as hi + lo bf16.
+template <bool COUNT>
+__global__ __launch_bounds__(1024) void set_union(
+    const int32_t* __restrict__ eord, const int32_t* __restrict__ n_uniq,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ seg, int K, int L,
+    const int32_t* __restrict__ stoff, const float* __restrict__ dh, const float* __restrict__ ga,
+    int32_t* __restrict__ nS, int32_t* __restrict__ T, uint16_t* __restrict__ dht_hi,
+    uint16_t* __restrict__ dht_lo, uint16_t* __restrict__ gat_hi, uint16_t* __restrict__ gat_lo) {
+  extern __shared__ unsigned bm[];  // W bitmap words, then their prefix
+  __shared__ int wtot[16];
+  const int W = (L + 31) / 32;
+  unsigned* pre = bm + W;
+  const int n = *n_uniq, nsets = (n + BT - 1) / BT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cw = (W + 1023) / 1024;  // prefix: thread tid owns words [tid cw, tid cw + cw)
+  for (int si = blockIdx.x; si < nsets; si += gridDim.x) {
+    for (int i = tid; i < W; i += 1024) bm[i] = 0u;
+    __syncthreads();
+    for (int r = wv; r < BT && si * BT + r < n; r += 16) {  // wave: experts r, r + 16, ...
+      const int u = eord[si * BT + r];
+      for (int i = seg[u] + lane; i < seg[u + 1]; i += 64) {
+        const int t = perm[i] / K;
+        atomicOr(&bm[t >> 5], 1u << (t & 31));
       }
     }
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, e0);
-    if (kt + 1 < nk) step(kt + 1, e1);
-  }
+    __syncthreads();
+    int loc = 0;
+    for (int w = tid * cw; w < min(W, tid * cw + cw); ++w) loc += __popc(bm[w]);
+    const int inc = wave_incl_scan(loc);
+    if (lane == 63) wtot[wv] = inc;
+    __syncthreads();
+    int run = inc - loc, ns = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = i * 16 + 4 * (lane >> 4) + e;
-      const int t = slot_token(order, b * BT + r, L);
-      if (t < 0) continue;
-      float* yr = y + (size_t)t * d + c0 + wave * 64 + (lane & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) yr[q * 16] = acc[i][q][e];
+    for (int w = 0; w < 16; ++w) {
+      run += w < wv ? wtot[w] : 0;
+      ns += wtot[w];
     }
+    for (int w = tid * cw; w < min(W, tid * cw + cw); ++w) {
+      pre[w] = run;
+      run += __popc(bm[w]);
+    }
+    if constexpr (COUNT) {
+      if (tid == 0) nS[si] = ns;
+      __syncthreads();  // wtot and the bitmap are reused by the next set
+      continue;
+    }
+    __syncthreads();
+    const int npad = (stoff[si + 1] - stoff[si]) * UPAD;
+    int32_t* Ts = T + (size_t)stoff[si] * UPAD;
+    for (int w = tid; w < W; w += 1024) {
+      unsigned bits = bm[w];
+      int r0 = pre[w];
+      while (bits) {
+        Ts[r0++] = w * 32 + __builtin_ctz(bits);
+        bits &= bits - 1u;
+      }
+    }
+    for (int c = ns + tid; c < npad; c += 1024) Ts[c] = 0;
+    const size_t go = (size_t)stoff[si] * BT * UPAD;
+    const int n8 = BT * npad / 8;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < n8; i += 1024) {
+      ((u32x4*)(dht_hi + go))[i] = z;
+      ((u32x4*)(dht_lo + go))[i] = z;
+      ((u32x4*)(gat_hi + go))[i] = z;
+      ((u32x4*)(gat_lo + go))[i] = z;
+    }
+    __syncthreads();  // the fill is complete before the tasks land on it
+    for (int r = wv; r < BT && si * BT + r < n; r += 16) {
+      const int u = eord[si * BT + r];
+      for (int i = seg[u] + lane; i < seg[u + 1]; i += 64) {
+        const int m = perm[i], t = m / K;
+        const int c = pre[t >> 5] + __popc(bm[t >> 5] & ((1u << (t & 31)) - 1u));
+        const size_t o = go + (size_t)r * npad + c;
+        const float a = dh[m], g = ga[m];
+        const uint16_t ah = bf16_rne(a), gh = bf16_rne(g);
+        dht_hi[o] = ah;
+        dht_lo[o] = bf16_rne(a - __uint_as_float((uint32_t)ah << 16));
+        gat_hi[o] = gh;
+        gat_lo[o] = bf16_rne(g - __uint_as_float((uint32_t)gh << 16));
+      }
+    }
+    __syncthreads();  // the bitmap is cleared for the next set only after every use
+  }
+}
+
+// stoff[s] = column tiles of the sets before s, for the ceil(n_uniq / 64)
+// sets (the capacity slots past them have none); stoff[smax] = all tiles
+__global__ __launch_bounds__(1024) void set_plan(const int32_t* __restrict__ nS,
+                                                 const int32_t* __restrict__ n_uniq, int smax,
+                                                 int32_t* __restrict__ stoff) {
+  __shared__ int wtot[16];
+  const int tid = threadIdx.x;
+  const int nsets = (*n_uniq + BT - 1) / BT;
+  int carry = 0;
+  for (int base = 0; base < smax; base += 1024) {
+    const int si = base + tid;
+    const int tiles = si < nsets ? max(1, (nS[si] + UPAD - 1) / UPAD) : 0;
+    const int inc = wave_incl_scan(tiles);
+    if ((tid & 63) == 63) wtot[tid >> 6] = inc;
+    __syncthreads();
+    int off = inc - tiles, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      off += w < (tid >> 6) ? wtot[w] : 0;
+      tot += wtot[w];
+    }
+    if (si < smax) stoff[si] = carry + off;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) stoff[smax] = carry;
 }
 
 constexpr int MI355X_CUS = 256;
@@ -576,22 +828,22 @@ BlockedPlan plan_blocked(int64_t L, int64_t K, int64_t N) {
   return p;
 }
 
-hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, const int32_t* idx,
-                                 const float* gate, const int32_t* order, int L, int d, int K,
-                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s) {
+namespace {
+
+// blk_union (with the task-slot map when kmap is not null) and blk_plan
+hipError_t launch_union_plan(const int32_t* idx, const float* gate, const int32_t* order, int L,
+                             int K, const BlockedPlan& p, void* ws, int32_t* kmap, hipStream_t s) {
   char* w = (char*)ws;
   int32_t* U = (int32_t*)(w + p.off_U);
   int32_t* nU = (int32_t*)(w + p.off_nU);
   int32_t* toff = (int32_t*)(w + p.off_toff);
   float* G = (float*)(w + p.off_G);
-  uint16_t* Ahi = (uint16_t*)(w + p.off_Ahi);
-  uint16_t* Alo = (uint16_t*)(w + p.off_Alo);
   const size_t lds_u = (size_t)(p.sort_keys + 1024) * 4;  // keys and one pad word per thread
   switch (p.sort_keys / 1024) {
 #define OMNI_BLK_UNION(E)                                                                     \
   case E:                                                                                     \
     hipLaunchKernelGGL(blk_union<E>, dim3(p.nb), dim3(1024), lds_u, s, idx, gate, order, L, \
-                       K, p.ucap, U, nU, G);                                                  \
+                       K, p.ucap, U, nU, G, kmap);                                            \
     break;
     OMNI_BLK_UNION(1) OMNI_BLK_UNION(2) OMNI_BLK_UNION(4) OMNI_BLK_UNION(8) OMNI_BLK_UNION(16)
     OMNI_BLK_UNION(32)
@@ -600,13 +852,154 @@ hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, co
       return hipErrorInvalidValue;  // K above the validated limit
   }
   hipLaunchKernelGGL(blk_plan, dim3(1), dim3(1024), 0, s, nU, p.nb, toff);
+  return hipGetLastError();
+}
+
+int act_grid(const BlockedPlan& p) {
   const int max_tiles = p.nb * (p.ucap / UPAD);
-  const int k1_grid = 8 * std::min((max_tiles + 7) / 8, MI355X_CUS * K1_WG_PER_CU / 8);
-  hipLaunchKernelGGL(blk_act, dim3(k1_grid), dim3(256), K1_S * K1_STAGE, s,
-                     (const uint16_t*)x, (const uint16_t*)W, order, U, toff, G, L, d, p.nb, p.ucap,
-                     Ahi, Alo);
-  hipLaunchKernelGGL(blk_out, dim3(p.nb * (d / K2_COLS)), dim3(256), K2_S * K2_STAGE, s,
-                     (const uint16_t*)V, order, U, toff, Ahi, Alo, L, d, p.ucap, y);
+  return 8 * std::min((max_tiles + 7) / 8, MI355X_CUS * K1_WG_PER_CU / 8);
+}
+
+// dy = dy_hi + dy_lo, two bf16 terms (round to nearest even, then the rest)
+__global__ __launch_bounds__(256) void split_bf16(const float* __restrict__ a, size_t n,
+                                                  uint16_t* __restrict__ hi,
+                                                  uint16_t* __restrict__ lo) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const float v = a[i];
+    const uint16_t h = bf16_rne(v);
+    hi[i] = h;
+    lo[i] = bf16_rne(v - __uint_as_float((uint32_t)h << 16));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, const int32_t* idx,
+                                 const float* gate, const int32_t* order, int L, int d, int K,
+                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  const int32_t* U = (const int32_t*)(w + p.off_U);
+  const int32_t* toff = (const int32_t*)(w + p.off_toff);
+  const float* G = (const float*)(w + p.off_G);
+  uint16_t* Ahi = (uint16_t*)(w + p.off_Ahi);
+  uint16_t* Alo = (uint16_t*)(w + p.off_Alo);
+  hipError_t e = launch_union_plan(idx, gate, order, L, K, p, ws, nullptr, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(blk_act<BLK_FWD>, dim3(act_grid(p)), dim3(256), K1_S * K1_STAGE, s,
+                     (const uint16_t*)x, (const uint16_t*)W, nullptr, nullptr, nullptr, order, U,
+                     toff, G, nullptr, L, d, K, p.nb, p.ucap, Ahi, Alo, nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL((blk_out<false, 1, false>), dim3(p.nb * (d / K2_COLS)), dim3(256),
+                     K2_S * K2_STAGE, s, (const uint16_t*)V, nullptr, order, nullptr, U, toff, Ahi,
+                     Alo, L, d, p.ucap, (void*)y);
+  return hipGetLastError();
+}
+
+BlockedBwdPlan plan_expert_backward_blocked(int64_t L, int64_t d, int64_t N, int64_t K) {
+  BlockedBwdPlan p{};
+  p.blk = plan_blocked(L, K, N);
+  p.bwd = plan_expert_backward(L, d, N, K);
+  const int64_t M = L * K;
+  p.ucap_e = (int)std::min<int64_t>(N, M);
+  p.smax = (p.ucap_e + BT - 1) / BT;
+  p.ksort = plan_schedule(p.ucap_e, 1, L + 1, 1);
+  // the sets' unions hold at most min(L, tasks) tokens each, in whole tiles
+  const size_t tcap = (size_t)M + (size_t)UPAD * p.smax;
+  p.set_elems = (size_t)BT * tcap;
+  auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  size_t o = 0;
+  p.off_blk = o;    o += a256(p.blk.ws_bytes);
+  p.off_kmap = o;   o += a256((size_t)p.blk.nb * BT * p.blk.ucap * 4);
+  p.off_dyh = o;    o += a256((size_t)L * d * 2);
+  p.off_dyl = o;    o += a256((size_t)L * d * 2);
+  p.off_bwd = o;    o += a256(p.bwd.ws_bytes);
+  p.off_pos = o;    o += a256((size_t)L * 4);
+  p.off_key = o;    o += a256((size_t)p.ucap_e * 4);
+  p.off_eord = o;   o += a256((size_t)p.ucap_e * 4);
+  p.off_ksort = o;  o += a256(p.ksort.ws_bytes);
+  p.off_ns = o;     o += a256((size_t)p.smax * 4);
+  p.off_stoff = o;  o += a256((size_t)(p.smax + 1) * 4);
+  p.off_T = o;      o += a256(tcap * 4);
+  p.off_dht = o;    o += 2 * a256(p.set_elems * 2);
+  p.off_gat = o;    o += 2 * a256(p.set_elems * 2);
+  p.ws_bytes = o;
+  return p;
+}
+
+hipError_t launch_expert_backward_blocked(const void* x, const void* W, const void* V,
+                                          const int32_t* idx, const float* gate, const float* dy,
+                                          const int32_t* order, int L, int d, int N, int K,
+                                          float* dx, float* dgate, int32_t* uniq, int32_t* n_uniq,
+                                          omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                          const BlockedBwdPlan& p, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  char* wb = w + p.off_blk;
+  const BlockedPlan& bp = p.blk;
+  const int32_t* U = (const int32_t*)(wb + bp.off_U);
+  const int32_t* toff = (const int32_t*)(wb + bp.off_toff);
+  const float* G = (const float*)(wb + bp.off_G);
+  uint16_t* dHhi = (uint16_t*)(wb + bp.off_Ahi);
+  uint16_t* dHlo = (uint16_t*)(wb + bp.off_Alo);
+  int32_t* kmap = (int32_t*)(w + p.off_kmap);
+  uint16_t* dyh = (uint16_t*)(w + p.off_dyh);
+  uint16_t* dyl = (uint16_t*)(w + p.off_dyl);
+  char* wr = w + p.off_bwd;
+  float* dh = (float*)(wr + p.bwd.off_dh);
+  float* ga = (float*)(wr + p.bwd.off_ga);
+  const int32_t* perm = (const int32_t*)(wr + p.bwd.off_perm);
+  const int32_t* seg = (const int32_t*)(wr + p.bwd.off_seg);
+  int32_t* pos = (int32_t*)(w + p.off_pos);
+  int32_t* key = (int32_t*)(w + p.off_key);
+  int32_t* eord = (int32_t*)(w + p.off_eord);
+  int32_t* nS = (int32_t*)(w + p.off_ns);
+  int32_t* stoff = (int32_t*)(w + p.off_stoff);
+  int32_t* T = (int32_t*)(w + p.off_T);
+  const size_t term = ((p.set_elems * 2) + 255) & ~(size_t)255;
+  uint16_t* dht_hi = (uint16_t*)(w + p.off_dht);
+  uint16_t* dht_lo = (uint16_t*)(w + p.off_dht + term);
+  uint16_t* gat_hi = (uint16_t*)(w + p.off_gat);
+  uint16_t* gat_lo = (uint16_t*)(w + p.off_gat + term);
+  // 1. per token block: dgate, the per-task terms dh and g SiLU(h), and dx
+  hipError_t e = launch_union_plan(idx, gate, order, L, K, bp, wb, kmap, s);
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)L * d;
+  hipLaunchKernelGGL(split_bf16, dim3((unsigned)std::min<size_t>((n + 255) / 256, 8192)), dim3(256),
+                     0, s, dy, n, dyh, dyl);
+  hipLaunchKernelGGL(blk_act<BLK_BWD>, dim3(act_grid(bp)), dim3(256), K1_S * K1_STAGE, s,
+                     (const uint16_t*)x, (const uint16_t*)W, dyh, dyl, (const uint16_t*)V, order, U,
+                     toff, G, kmap, L, d, K, bp.nb, bp.ucap, dHhi, dHlo, dgate, dh, ga);
+  // dx = dH W[U], the forward's second product with W in place of V
+  hipLaunchKernelGGL((blk_out<false, 1, false>), dim3(bp.nb * (d / K2_COLS)), dim3(256),
+                     K2_S * K2_STAGE, s, (const uint16_t*)W, nullptr, order, nullptr, U, toff, dHhi,
+                     dHlo, L, d, bp.ucap, (void*)dx);
+  // 2. the used experts, then the expert sets and their dW, dV rows
+  if ((e = launch_expert_segments(idx, N, uniq, n_uniq, p.bwd, wr, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(inv_order, dim3((L + 255) / 256), dim3(256), 0, s, order, L, pos);
+  hipLaunchKernelGGL(set_keys, dim3((unsigned)std::min(2048, (p.ucap_e + 3) / 4)), dim3(256), 0, s,
+                     perm, seg, n_uniq, pos, K, L, p.ucap_e, key);
+  if ((e = launch_sort_keys(key, p.ucap_e, (int64_t)L + 1, eord, w + p.off_ksort, s)) != hipSuccess)
+    return e;
+  const size_t lds_s = (size_t)2 * ((L + 31) / 32) * 4;
+  const dim3 sgrid((unsigned)std::min(p.smax, MI355X_CUS));
+  hipLaunchKernelGGL(set_union<true>, sgrid, dim3(1024), lds_s, s, eord, n_uniq, perm, seg, K, L,
+                     nullptr, nullptr, nullptr, nS, nullptr, nullptr, nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL(set_plan, dim3(1), dim3(1024), 0, s, nS, n_uniq, p.smax, stoff);
+  hipLaunchKernelGGL(set_union<false>, sgrid, dim3(1024), lds_s, s, eord, n_uniq, perm, seg, K, L,
+                     stoff, dh, ga, nullptr, T, dht_hi, dht_lo, gat_hi, gat_lo);
+  const bool obf = grad_dt == OMNI_BF16;
+  const dim3 ogrid((unsigned)std::min(p.smax * (d / K2_COLS), 2 * MI355X_CUS));
+  const dim3 ogrid2((unsigned)std::min(p.smax * (d / K2_COLS), MI355X_CUS));
+  constexpr size_t lds1 = K2_S * (K2_VT + 2 * K2_AT), lds2 = K2_S * (2 * K2_VT + 2 * K2_AT);
+  if (obf) {
+    hipLaunchKernelGGL((blk_out<true, 1, true>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows);
+    hipLaunchKernelGGL((blk_out<true, 2, true>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord, n_uniq,
+                       T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows);
+  } else {
+    hipLaunchKernelGGL((blk_out<true, 1, false>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows);
+    hipLaunchKernelGGL((blk_out<true, 2, false>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord,
+                       n_uniq, T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows);
+  }
   return hipGetLastError();
 }
 

@@ -160,6 +160,10 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
                            int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
+// order[0..M) = 0..M-1 stably sorted by keys[i] in [0, key_bound); workspace
+// plan_schedule(M, 1, key_bound, 1).ws_bytes
+hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
+                            void* ws, hipStream_t s);
 // order[0..L) = the tokens stably sorted by idx[t*K] / B (the group of each
 // token's first expert); uses the schedule's workspace (plan_schedule(L, K, ..)
 // covers it)
@@ -184,6 +188,7 @@ hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act
 constexpr int BLK_TOKENS = 64;       // tokens per block (consecutive entries of the order)
 constexpr int BLK_UNION_TILE = 128;  // union columns per tile
 constexpr int BLK_D_TILE = 256;      // y columns per output tile (d must be a multiple)
+constexpr int BLK_BWD_MAX_L = 524288;  // tokens of the backward's LDS bitmap (128 KB)
 struct BlockedPlan {
   int nb, ucap, sort_keys;  // blocks, union capacity per block, LDS sort size
   size_t off_U, off_nU, off_toff, off_G, off_Ahi, off_Alo, ws_bytes;
@@ -213,12 +218,42 @@ struct BwdPlan {
   size_t off_dh, off_ga, off_perm, off_eoff, off_seg, off_cnt, off_sched, ws_bytes;
 };
 BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K);
+// the tasks sorted by expert (the plan's perm), the used experts (uniq,
+// n_uniq) and each one's first position in the sorted tasks (the plan's seg,
+// seg[n_uniq] = L*K)
+hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int32_t* n_uniq,
+                                  const BwdPlan& p, void* ws, hipStream_t s);
+// used experts and their dW / dV rows from the per-task terms dh, ga that
+// the plan's workspace already holds (the second half of the backward)
+hipError_t launch_expert_grad_rows(const void* x, const float* dy, const int32_t* idx, int L, int d,
+                                   int N, int K, omni_dtype dt, int32_t* uniq, int32_t* n_uniq,
+                                   omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                   const BwdPlan& p, void* ws, hipStream_t s);
 // dx (expert part, overwritten), dgate, used experts and their dW / dV rows
 hipError_t launch_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
                                   const float* gate, const float* dy, int L, int d, int N, int K,
                                   omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
                                   int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s);
+
+// the blocked form of the backward: dgate, the per-task terms and dx by
+// dense products over the forward's token blocks, then the rows as above
+struct BlockedBwdPlan {
+  BlockedPlan blk;
+  BwdPlan bwd;
+  SchedPlan ksort;  // the sort of the used experts by their first token position
+  int ucap_e, smax;  // used-expert capacity, expert-set capacity
+  size_t off_blk, off_kmap, off_dyh, off_dyl, off_bwd;
+  size_t off_pos, off_key, off_eord, off_ksort, off_ns, off_stoff, off_T, off_dht, off_gat;
+  size_t set_elems, ws_bytes;  // dense set-tile capacity (elements per matrix and term)
+};
+BlockedBwdPlan plan_expert_backward_blocked(int64_t L, int64_t d, int64_t N, int64_t K);
+hipError_t launch_expert_backward_blocked(const void* x, const void* W, const void* V,
+                                          const int32_t* idx, const float* gate, const float* dy,
+                                          const int32_t* order, int L, int d, int N, int K,
+                                          float* dx, float* dgate, int32_t* uniq, int32_t* n_uniq,
+                                          omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                          const BlockedBwdPlan& p, void* ws, hipStream_t s);
 
 struct RouterBwdPlan {
   int Ntot_p, L_p;

@@ -249,6 +249,13 @@ hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedP
   return hipGetLastError();
 }
 
+hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
+                            void* ws, hipStream_t s) {
+  const SchedPlan plan = plan_schedule(M, 1, key_bound, 1);
+  sort_by_group(keys, 1, M, 1, plan, order, ws, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
                               int32_t* order, void* ws, hipStream_t s) {
   // the plan for L elements needs no more workspace than the one for L*K

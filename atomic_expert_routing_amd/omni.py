@@ -16,14 +16,15 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 6
+_ABI_VERSION = 7
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
-OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED = 6, 7
+OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED, OMNI_OP_EXPERT_BACKWARD_BLOCKED = 6, 7, 8
 EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
+            "omni_expert_backward_blocked",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
             "omni_shared_mlp", "omni_dense_router", "omni_workspace_bytes", "omni_status_string",
             "omni_last_error", "omni_abi_version")
@@ -61,6 +62,9 @@ def library() -> ctypes.CDLL:
     lib.omni_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp,
                                          vp, sz, vp]
+    lib.omni_expert_backward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                 ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp,
+                                                 vp, vp, sz, vp]
     lib.omni_router_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.omni_shared_mlp.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp,
@@ -70,6 +74,7 @@ def library() -> ctypes.CDLL:
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
     for f in ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
+              "omni_expert_backward_blocked",
               "omni_expert_forward_token_centric", "omni_expert_backward",
               "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
               "omni_workspace_bytes"):
@@ -265,6 +270,21 @@ def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None,
     U_cap = min(N, L*K); only the first n_uniq entries / rows are defined.
     The gradient rows are float32 or bfloat16 (grad_dtype).
     """
+    return _expert_backward(None, x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq, dW_rows,
+                            dV_rows, ws, stream, grad_dtype)
+
+
+def omni_expert_backward_blocked(x, W, V, idx, gate, dy, token_order, dx=None, dgate=None,
+                                 uniq=None, n_uniq=None, dW_rows=None, dV_rows=None, ws=None,
+                                 stream=None, grad_dtype=torch.float32):
+    """omni_expert_backward with the per-token part over the blocked
+    assembly's token blocks (token_order: [L] int32); same returns."""
+    return _expert_backward(token_order, x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq,
+                            dW_rows, dV_rows, ws, stream, grad_dtype)
+
+
+def _expert_backward(token_order, x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq, dW_rows,
+                     dV_rows, ws, stream, grad_dtype):
     L, d = x.shape
     N = W.shape[0]
     K = idx.shape[1]
@@ -285,9 +305,17 @@ def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None,
             _dev(dgate, "dgate", f32, (L, K)), _dev(uniq, "uniq", i32, (cap,)),
             _dev(n_uniq, "n_uniq", i32, (1,)), _dtype_code(dW_rows),
             _dev(dW_rows, "dW_rows", gdt, (cap, d)), _dev(dV_rows, "dV_rows", gdt, (cap, d)))
-    need = omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
+    op = OMNI_OP_EXPERT_BACKWARD if token_order is None else OMNI_OP_EXPERT_BACKWARD_BLOCKED
+    need = omni_workspace_bytes(op, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
     pw, nw = _workspace(ws, need, x.device)
-    _check(library().omni_expert_backward(*args, pw, nw, _stream(stream)), "omni_expert_backward")
+    if token_order is None:
+        _check(library().omni_expert_backward(*args, pw, nw, _stream(stream)),
+               "omni_expert_backward")
+    else:
+        po = _dev(token_order, "token_order", i32, (L,))
+        _check(library().omni_expert_backward_blocked(*args[:6], po, *args[6:], pw, nw,
+                                                      _stream(stream)),
+               "omni_expert_backward_blocked")
     return dx, dgate, uniq, n_uniq, dW_rows, dV_rows
 
 

@@ -338,6 +338,30 @@ def time_backward(inp, w, br, steps, seed):
         run(e, rows=(dW16, dV16))
     torch.cuda.synchronize()
     exp16_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs16)
+    blocked_ms = None
+    if w.dtype == "bf16" and d % 256 == 0:
+        # the blocked form, over the schedule's token order (fp32 rows)
+        _, _, order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True)
+        ws_b = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_BLOCKED, L, d,
+                                                     1, 1, K, N, 1, dt),
+                           dtype=torch.uint8, device="cuda")
+
+        def run_blocked():
+            omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                              order, dx, dgate, uniq, n_uniq, dW, dV, ws_b)
+
+        run_blocked()
+        torch.cuda.synchronize()
+        tb = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run_blocked()
+            e1.record()
+            tb.append((e0, e1))
+        torch.cuda.synchronize()
+        blocked_ms = statistics.median(a.elapsed_time(b) for a, b in tb)
+        del ws_b
     U = int(n_uniq.item())
     es = 2 if w.dtype == "bf16" else 4
     # unique W and V rows read, their fp32 dW and dV rows written; x and dy
@@ -348,6 +372,7 @@ def time_backward(inp, w, br, steps, seed):
     return {
         "expert_backward_ms": round(exp_ms, 4),
         "expert_backward_bf16_rows_ms": round(exp16_ms, 4),
+        "expert_backward_blocked_ms": None if blocked_ms is None else round(blocked_ms, 4),
         "expert_backward_bf16_rows_hbm_frac": round(
             exp16_bytes / (exp16_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "router_backward_ms": round(rt_ms, 4),

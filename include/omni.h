@@ -12,6 +12,7 @@
  * omni_expert_forward_token_centric.
  * The backward of the branch runs in two more calls:
  *   omni_expert_backward  dx (expert part), d gate, dW and dV of used experts
+ *                         (omni_expert_backward_blocked: its blocked form)
  *   omni_router_backward  dW_r, dW_c, and the router part added into dx
  * and the layer's other branch in one:
  *   omni_shared_mlp       the shared dense MLP, added into (or written to) y
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 6
+#define OMNI_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -73,7 +74,8 @@ typedef enum {
   OMNI_OP_ROUTER_BACKWARD = 4,
   OMNI_OP_SHARED_MLP = 5, /* omni_workspace_bytes takes d_ff in its N argument */
   OMNI_OP_DENSE_ROUTER = 6,
-  OMNI_OP_EXPERT_FORWARD_BLOCKED = 7
+  OMNI_OP_EXPERT_FORWARD_BLOCKED = 7,
+  OMNI_OP_EXPERT_BACKWARD_BLOCKED = 8
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -267,6 +269,39 @@ OMNI_API omni_status omni_expert_backward(const void* x, const void* W, const vo
                                           int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
                                           void* dV_rows, void* ws, size_t ws_bytes,
                                           void* stream);
+
+/*
+ * omni_expert_backward_blocked - the same gradients as omni_expert_backward,
+ * with the per-token part (dgate, the per-task terms and dx) computed over
+ * the blocked assembly's token blocks: for block b (64 consecutive entries
+ * of token_order) and the union U_b of its experts,
+ *   H = X_b W[U_b]^T,  D = dy_b V[U_b]^T      (dense MFMA products)
+ *   at each task: dgate = D SiLU(h), dh = g D SiLU'(h), g SiLU(h)
+ *   dx_b = dH W[U_b]                          (dH: dh at the tasks, else 0)
+ * dy enters the MFMA products as two bf16 terms (hi + lo, about 16
+ * significant bits), dH likewise; sums are fp32.  For routing in which many
+ * tokens share experts; on spread-out routing omni_expert_backward is faster.
+ *   token_order [L] int32  a permutation of [0, L), as for
+ *                          omni_expert_forward_blocked
+ * The dW and dV rows are summed over sets of 64 used experts (ordered by the
+ * first position of their tokens in token_order) as dense products with the
+ * union of the set's tokens: dW rows = DhT X[T_s], dV rows = GaT dy[T_s],
+ * each row written once (deterministic; the summation order differs from
+ * omni_expert_backward's, so the rows agree to fp32 rounding).
+ * Other arguments, outputs and limits as omni_expert_backward, plus those of
+ * omni_expert_forward_blocked (bf16, d % 256 == 0, distinct ids per token)
+ * and L <= 524288.
+ * Workspace: omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD_BLOCKED).
+ */
+OMNI_API omni_status omni_expert_backward_blocked(const void* x, const void* W, const void* V,
+                                                  const int32_t* idx, const float* gate,
+                                                  const float* dy, const int32_t* token_order,
+                                                  int64_t L, int64_t d, int64_t N, int64_t K,
+                                                  omni_dtype dt, float* dx, float* dgate,
+                                                  int32_t* uniq, int32_t* n_uniq,
+                                                  omni_dtype grad_dt, void* dW_rows,
+                                                  void* dV_rows, void* ws, size_t ws_bytes,
+                                                  void* stream);
 
 /*
  * omni_router_backward - gradients of the Cartesian Product Router.

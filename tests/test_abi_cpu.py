@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 6
+    assert lib.omni_abi_version() == 7
 
 
 def test_status_strings():
@@ -99,7 +99,7 @@ def test_schedule_validation():
         with pytest.raises(omni.OmniError):
             omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, **args)
     with pytest.raises(omni.OmniError):
-        omni.omni_workspace_bytes(8)
+        omni.omni_workspace_bytes(9)
 
 
 def test_calls_reject_before_launch():
@@ -217,8 +217,36 @@ def test_blocked_workspace_and_validation():
         with pytest.raises(omni.OmniError) as e:
             omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, **args)
         assert e.value.status == st
+    # the blocked backward: the forward's workspace, the task-slot map (as G),
+    # dy split into two bf16 terms, then the per-task backward's workspace
+    # then the expert sets: positions, keys and the sorted order of the used
+    # experts (capacity min(N, L K)), the sort's buffers, per-set counts and
+    # tile prefix, the token unions and the dense hi/lo tiles of dh and g SiLU
+    for L, K, N, d in ((16384, 256, 1700416, 2048), (100, 16, 1024, 256)):
+        nb = -(-L // 64)
+        ucap = -(-min(64 * K, N) // 128) * 128
+        fwd = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, L=L, d=d, K=K, N=N)
+        rows = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L=L, d=d, K=K, N=N)
+        ue = min(N, L * K)
+        smax = -(-ue // 64)
+        tcap = L * K + 128 * smax
+        got = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_BLOCKED, L=L, d=d, K=K, N=N)
+        head = a256(fwd) + a256(nb * 64 * ucap * 4) + 2 * a256(L * d * 2) + a256(rows)
+        tail = (a256(L * 4) + 2 * a256(ue * 4) + a256(smax * 4) + a256((smax + 1) * 4)
+                + a256(tcap * 4) + 4 * a256(64 * tcap * 2))
+        sort = got - head - tail  # the key sort's buffers: two key and value arrays and more
+        assert 4 * ue * 4 <= sort <= 4 * a256(ue * 4) + 1 << 20, (L, K, N, sort)
+    for kw in (dict(d=320), dict(L=524289)):
+        args = dict(L=64, d=256, K=8, N=100)
+        args.update(kw)
+        with pytest.raises(omni.OmniError):
+            omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_BLOCKED, **args)
     lib = omni.library()
     fake = ctypes.c_void_p(4096)
+    s = lib.omni_expert_backward_blocked(fake, fake, fake, fake, fake, fake, None, 64, 256, 1000,
+                                         8, omni.OMNI_BF16, fake, fake, fake, fake, omni.OMNI_F32,
+                                         fake, fake, fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
     # the token order is required
     s = lib.omni_expert_forward_blocked(fake, fake, fake, fake, fake, None, 64, 256, 1000, 8,
                                         omni.OMNI_BF16, fake, fake, 1 << 30, None)

@@ -184,3 +184,77 @@ def test_full_size_backward_sampled(name):
     say(f"  dWr err {nr[0]:.1e} dWc err {nc[0]:.1e}")
     del inp, br, g
     torch.cuda.empty_cache()
+
+
+BLOCKED_CASES = [
+    (64, 256, 32, 32, 16),
+    (130, 256, 37, 29, 50),   # ragged last block, unions over several column tiles
+    (1, 256, 4, 4, 3),        # one token
+    (200, 512, 20, 20, 1),    # K = 1
+    (65, 256, 30, 30, 512),   # K at its limit
+    (96, 2048, 40, 40, 128),
+]
+
+
+@pytest.mark.parametrize("case", BLOCKED_CASES, ids=lambda c: "L{}_d{}_{}x{}_K{}".format(*c))
+def test_blocked_backward_matches_oracle(case):
+    """omni_expert_backward_blocked on the oracle's routing: against the
+    backward oracle (fp32-arithmetic bound) and, bit for bit where the two
+    share the summation (uniq, n_uniq), against omni_expert_backward."""
+    L, d, Nr, Nc, K = case
+    say(f"blocked backward case {case}")
+    w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, 8, "bf16", seed=4)
+    idx_o, _, gate_o, _, _ = O.route(inp_cpu["x"], inp_cpu["Wr"], inp_cpu["Wc"], K)
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    idx = torch.as_tensor(idx_o, dtype=torch.int32).cuda()
+    gate = torch.as_tensor(gate_o, dtype=torch.float32).cuda()
+    dy = synth.upstream_grad(w, seed=4).cuda()
+    _, _, order = omni.omni_schedule(idx, w.N, w.B, token_order=True)
+    dx, dgate, uniq, n_uniq, dW, dV = omni.omni_expert_backward_blocked(
+        inp["x"], inp["W"], inp["V"], idx, gate, dy, order)
+    ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], idx, gate, dy)
+    torch.cuda.synchronize()
+    n = int(n_uniq.item())
+    assert n == int(ref[3].item())
+    assert torch.equal(uniq[:n], ref[2][:n])
+    gate_f = to_np(gate).astype(np.float64)
+    dy_c = to_np(dy).astype(np.float64)
+    terms = BO.task_terms(inp_cpu["x"], inp_cpu["W"], inp_cpu["V"], idx_o, gate_f, dy_c)
+    uniq_o = np.unique(idx_o)
+    dW_o, dV_o = BO.expert_grads(inp_cpu["x"], dy_c, idx_o, terms, uniq_o)
+    dx_o = BO.input_grad_expert(inp_cpu["W"], idx_o, terms["dh"])
+    errs = {"dgate": check_y(dgate, terms["dgate"].reshape(L, K), RTOL_FP32_ARITH),
+            "dx": check_y(dx, dx_o, RTOL_FP32_ARITH),
+            "dW": check_y(to_np(dW)[:n], dW_o, RTOL_FP32_ARITH),
+            "dV": check_y(to_np(dV)[:n], dV_o, RTOL_FP32_ARITH)}
+    say("  " + " ".join(f"{k}={v[0]:.1e}" for k, v in errs.items()))
+    # deterministic: a second call reproduces every output bit for bit
+    again = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], idx, gate, dy, order)
+    torch.cuda.synchronize()
+    for a, b in zip((dx, dgate, dW[:n], dV[:n]), (again[0], again[1], again[4][:n], again[5][:n])):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["skewed_L16384_N1700416_d2048", synth.HEADLINE])
+def test_blocked_backward_full_size(name):
+    """Both full-size workloads: every output of the blocked backward against
+    the per-task backward on the same routing (norm-wise, fp32 bound)."""
+    w = synth.WORKLOADS[name]
+    say(f"blocked backward full-size {name}")
+    inp = synth.make_inputs(w, seed=0, device="cuda")
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True)
+    br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    dy = synth.upstream_grad(w, seed=0, device="cuda")
+    ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy)
+    got = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                            br.token_order)
+    torch.cuda.synchronize()
+    n = int(ref[3].item())
+    assert int(got[3].item()) == n and torch.equal(got[2][:n], ref[2][:n])
+    for name_, a, b in (("dx", got[0], ref[0]), ("dgate", got[1], ref[1]),
+                        ("dW", got[4][:n], ref[4][:n]), ("dV", got[5][:n], ref[5][:n])):
+        rel = ((a - b).norm() / b.norm()).item()
+        say(f"  {name_}: rel diff {rel:.2e}")
+        assert rel <= RTOL_FP32_ARITH, name_
+    del inp, br, ref, got
+    torch.cuda.empty_cache()
