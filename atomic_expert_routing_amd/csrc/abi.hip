@@ -199,14 +199,21 @@ omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K, int64_t N, i
   size_t need = 0;
   omni_status s = schedule_ws(L, K, N, B, &need);
   if (s != OMNI_OK) return s;
-  if (!idx || !perm || !group_off) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL array pointer");
+  if (!idx) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL idx");
+  if (!perm != !group_off)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: perm and group_off go together");
+  if (!perm && !token_order) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: no output");
   if (token_order && L > I32_LIMIT - 7)
     return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  const omni::SchedPlan plan = omni::plan_schedule(L, K, N, B);
-  hipError_t e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws, st);
-  if (e != hipSuccess || !token_order) return hip_status(e, "schedule launch");
+  hipError_t e = hipSuccess;
+  if (perm) {
+    const omni::SchedPlan plan = omni::plan_schedule(L, K, N, B);
+    e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws, st);
+    if (e != hipSuccess) return hip_status(e, "schedule launch");
+  }
+  if (!token_order) return ok();
   e = omni::launch_token_order(idx, (int)L, (int)K, N, (int)B, token_order, ws, st);
   return hip_status(e, "token order launch");
 }

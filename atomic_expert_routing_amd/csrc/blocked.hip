@@ -26,6 +26,19 @@
 //              written as two bf16 terms hi + lo (about 16 significant bits)
 //   blk_out    y_b = (A_hi + A_lo) V[U_b], 64 x 256 MFMA tiles; the V rows
 //              pass through LDS, where the k-major operand is read transposed
+//
+// The backward (the chain rule of the same definition) reuses them:
+//   blk_union  also records each task's slot k at its (row, column)
+//   split_bf16 dy = dy_hi + dy_lo
+//   blk_act    (backward mode) H = X_b W[U_b]^T and D = dy_b V[U_b]^T in one
+//              pipeline; per task dgate = D SiLU(h), dh = g D SiLU'(h),
+//              g SiLU(h); the dense dH tile
+//   blk_out    dx_b = dH W[U_b]
+// and for the dW, dV rows groups the used experts into sets of 64 (experts
+// of one token cluster together), with each set's token union:
+//   inv_order, set_keys, a radix sort   the order of the used experts
+//   set_union, set_plan, set_union      the unions and dense tiles DhT, GaT
+//   blk_out    (set form) dW rows = DhT X[T_s], dV rows = GaT dy[T_s]
 
 #include <algorithm>
 #include <climits>
@@ -52,7 +65,8 @@ __device__ __forceinline__ int slot_token(const int32_t* __restrict__ order, int
 // thread for s < E (registers), in lane ^ (s / E) of the same wave for
 // E <= s < 64 E (lane exchanges, no barrier), and in another wave only for
 // s >= 64 E (through LDS, two barriers).
-// Compare-exchange of positions q and q ^ st (q < q ^ st), ascending if up.
+
+// Compare-exchange of positions q and j = q ^ st (q < j), ascending if up.
 template <int E>
 __device__ __forceinline__ void cas(int (&v)[E], int q, int j, bool up) {
   const int a = v[q], c = v[j];

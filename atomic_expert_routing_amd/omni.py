@@ -166,21 +166,25 @@ def omni_router(x, Wr, Wc, K: int, idx=None, score=None, gate=None, ws=None, str
 
 
 def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, stream=None,
-                  token_order=None):
+                  token_order=None, tasks=True):
     """Expert-centric schedule -> (perm [L*K] int32, group_off [G+1] int32).
 
     token_order: None (not computed), True (allocate) or an [L] int32 tensor;
     when given, the tokens sorted by the group of their first expert are
-    written there and returned as a third element.
+    written there and returned as a third element.  tasks=False computes the
+    token order alone (perm and group_off are returned as None).
     """
     L, K = idx.shape
     G = -(-N // B)
     pi = _dev(idx, "idx", torch.int32)
     kw = dict(device=idx.device, dtype=torch.int32)
-    perm = torch.empty((L * K,), **kw) if perm is None else perm
-    group_off = torch.empty((G + 1,), **kw) if group_off is None else group_off
-    pp = _dev(perm, "perm", torch.int32, (L * K,))
-    po = _dev(group_off, "group_off", torch.int32, (G + 1,))
+    if tasks:
+        perm = torch.empty((L * K,), **kw) if perm is None else perm
+        group_off = torch.empty((G + 1,), **kw) if group_off is None else group_off
+        pp = _dev(perm, "perm", torch.int32, (L * K,))
+        po = _dev(group_off, "group_off", torch.int32, (G + 1,))
+    else:
+        perm = group_off = pp = po = None
     need = omni_workspace_bytes(OMNI_OP_SCHEDULE, L, 8, 1, 1, K, N, B) if ws is None else 0
     if token_order is True:
         token_order = torch.empty((L,), **kw)
@@ -418,8 +422,9 @@ class RoutedBranch:
         return omni_router(x, Wr, Wc, self.K, self.idx, self.score, self.gate, self.ws, stream)
 
     def schedule(self, stream=None):
+        # the blocked assembly reads only the token order
         return omni_schedule(self.idx, self.N, self.B, self.perm, self.group_off, self.ws, stream,
-                             self.token_order)
+                             self.token_order, tasks=self.assembly != "blocked")
 
     def expert_forward(self, x, W, V, stream=None):
         if self.assembly == "blocked":

@@ -126,6 +126,10 @@ OMNI_API omni_status omni_router(const void* x, const void* Wr, const void* Wc,
  *                                  tasks whose group is < q, so group q's
  *                                  tasks are perm[group_off[q] .. group_off[q+1])
  *                                  (empty for an inactive group)
+ *                                  perm and group_off are both given or both
+ *                                  NULL (then only token_order is computed,
+ *                                  which is all omni_expert_forward_blocked
+ *                                  reads)
  *   token_order [L]     int32 out, optional (NULL: not computed)
  *                                  the tokens stably sorted by the group of
  *                                  their first expert, idx[t*K] / B (ties by

@@ -118,6 +118,11 @@ def test_calls_reject_before_launch():
     s = lib.omni_schedule(fake, 4, 2, 10, 2, fake, fake, None, ctypes.c_void_p(4100), 1 << 20,
                           None)
     assert s == omni.OMNI_ERR_INVALID_ARG
+    # perm without group_off, and no output at all
+    s = lib.omni_schedule(fake, 4, 2, 10, 2, fake, None, None, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"together" in lib.omni_last_error()
+    s = lib.omni_schedule(fake, 4, 2, 10, 2, None, None, None, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"no output" in lib.omni_last_error()
     # misaligned x
     s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, None, 4, 8,
                                 10, 2, omni.OMNI_BF16, fake, fake, 1 << 20, None)
