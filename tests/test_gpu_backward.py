@@ -233,6 +233,14 @@ def test_blocked_backward_matches_oracle(case):
     torch.cuda.synchronize()
     for a, b in zip((dx, dgate, dW[:n], dV[:n]), (again[0], again[1], again[4][:n], again[5][:n])):
         assert torch.equal(a, b)
+    # bf16 gradient rows: the same fp32 sums rounded to nearest even
+    b16 = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], idx, gate, dy, order,
+                                            grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert b16[4].dtype == torch.bfloat16 and int(b16[3].item()) == n
+    assert torch.equal(b16[4][:n], dW[:n].to(torch.bfloat16))
+    assert torch.equal(b16[5][:n], dV[:n].to(torch.bfloat16))
+    assert torch.equal(b16[0], dx) and torch.equal(b16[1], dgate)
 
 
 @pytest.mark.parametrize("name", ["skewed_L16384_N1700416_d2048", synth.HEADLINE])
