@@ -286,7 +286,11 @@ OMNI_API omni_status omni_expert_backward(const void* x, const void* W, const vo
  * significant bits), dH likewise; sums are fp32.  For routing in which many
  * tokens share experts; on spread-out routing omni_expert_backward is faster.
  *   token_order [L] int32  a permutation of [0, L), as for
- *                          omni_expert_forward_blocked
+ *                          omni_expert_forward_blocked; every token must
+ *                          appear once (a token that does not gets no dx row
+ *                          or dgate entries, and the dW, dV rows of its
+ *                          experts are undefined; entries outside [0, L) are
+ *                          skipped, nothing is accessed out of bounds)
  * The dW and dV rows are summed over sets of 64 used experts (ordered by the
  * first position of their tokens in token_order) as dense products with the
  * union of the set's tokens: dW rows = DhT X[T_s], dV rows = GaT dy[T_s],
