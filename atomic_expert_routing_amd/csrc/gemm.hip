@@ -192,8 +192,14 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
     }
 }
 
-// Two tile shapes, chosen per product by its tile count (measured on the
+// Three tile shapes, chosen per product by its tile count (measured on the
 // products this library runs; TFLOP/s on 2.5 PFLOP/s peak):
+//   huge:  256 x 256, 8 waves (4 x 2) of 64 x 128, BK = 64, 2 stages, 128 KB
+//          of LDS (one workgroup per CU).  Best when the product has at
+//          least two full rounds (512) of such tiles: 16384 x 2608 x 2048
+//          195 us (897; 224 us with the big tile), 4096 x 11008 x 2048 188 us
+//          (980; 202), 4096 x 65536 x 2048 1154 us (953; 1250).  On 4096 x
+//          2608 x 2048 (176 tiles) it takes 71 us against 58.
 //   big:   256 x 192, 8 waves (4 x 2) of 64 x 96, BK = 64, 2 stages, 112 KB
 //          of LDS (one workgroup per CU).  Best when the product has at
 //          least ~200 such tiles: 4096 x 2608 x 2048 56 us (776 TFLOP/s),
@@ -204,8 +210,13 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
 // Also measured and dropped: 128 x 192 (4 waves; 59 / 257 / 117 / 67 us on
 // the four products), 256 x 192 with 4 waves of 128 x 96 (BK 32 or 64, 2 or 3
 // stages: one wave per SIMD, 73-284 us), 256 x 256 with 8 waves and BK = 32,
-// 128 x 256.  Before the XCD-aware order the 128 x 128 tile took 64 us on the
-// router product (60 us after).
+// 128 x 256.  hipBLASLt (torch.matmul, bf16 out) takes 56 / 186 / 163 / 780 /
+// 84 us on 4096 x 2608 x 2048, 16384 x 2608 x 2048, 4096 x 11008 x 2048,
+// 4096 x 65536 x 2048 and 4096 x 2048 x 5504.  Before the XCD-aware order
+// the 128 x 128 tile took 64 us on the router product (60 us after).
+struct GemmCfgHuge {
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 8, MI = 4, WVM = 4, WVN = 2;
+};
 struct GemmCfgBig {
   static constexpr int BK = GEMM_KTILE, S = 2, NJ = 6, MI = 4, WVM = 4, WVN = 2;
 };
@@ -214,6 +225,7 @@ struct GemmCfgSmall {
 };
 using GemmCfg = GemmCfgBig;
 constexpr int GEMM_BIG_MIN_TILES = 200;
+constexpr int GEMM_HUGE_MIN_TILES = 512;  // two full rounds of 256 x 256 tiles
 
 // ------------------------------------------------------------------ fp32 product
 // C[m, n] (+)= sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk], 64 x 64 tiles.
@@ -287,7 +299,11 @@ template <int MODE>
 hipError_t launch_sel(const void* A, const void* B0, const void* B1, int n_split, int M, int N,
                       int Kd, float* C0, float* C1, int m_split, int ldc, bool accumulate,
                       uint16_t* Cb, hipStream_t s) {
+  const int huge_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int big_tiles = ((M + 255) / 256) * ((N + 191) / 192);
+  if (huge_tiles >= GEMM_HUGE_MIN_TILES)
+    return launch_t<MODE, GemmCfgHuge>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc,
+                                       accumulate, Cb, s);
   if (big_tiles >= GEMM_BIG_MIN_TILES)
     return launch_t<MODE, GemmCfgBig>(A, B0, B1, n_split, M, N, Kd, C0, C1, m_split, ldc,
                                       accumulate, Cb, s);
