@@ -354,6 +354,96 @@ __device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, u64* o
   }
 }
 
+// 64-bit wave max / min: the high words first, then the low words of the
+// lanes that hold the extreme high word.
+__device__ __forceinline__ u64 wave_umax64(u64 v) {
+  const unsigned hi = wave_umax((unsigned)(v >> 32));
+  const unsigned lo = wave_umax((unsigned)(v >> 32) == hi ? (unsigned)v : 0u);
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 wave_umin64(u64 v) {
+  const unsigned hi = wave_umin((unsigned)(v >> 32));
+  const unsigned lo = wave_umin((unsigned)(v >> 32) == hi ? (unsigned)v : 0xffffffffu);
+  return ((u64)hi << 32) | lo;
+}
+
+// Select the R largest of n unique nonzero 64-bit keys held in registers
+// (key[v] of a lane is element v*64 + lane; 0 pads the slots past n).  The
+// R-th largest key T is found bit by bit below the leading bits all keys
+// share, keeping count(>= T) >= R and stopping as soon as exactly R keys
+// qualify; being unique, exactly R keys are >= the final T.  They are
+// written to out[0..R) in element order.  Always inlined so that `out`
+// stays a known LDS pointer (DS instructions, no generic addressing).
+template <int Q>
+__device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[Q], int n, int R,
+                                                               u64* out) {
+  const int lane = threadIdx.x & 63;
+  const u64 lt = (1ull << lane) - 1ull;
+  u64 T = 1;  // R >= n: every key is taken
+  if (R < n) {
+    u64 mx = 0, mn = ~0ull;
+#pragma unroll
+    for (int v = 0; v < Q; ++v) {
+      mx = key[v] > mx ? key[v] : mx;
+      const u64 k = v * 64 + lane < n ? key[v] : ~0ull;
+      mn = k < mn ? k : mn;
+    }
+    mx = wave_umax64(mx);
+    mn = wave_umin64(mn);
+    const int hb = 63 - __clzll(mx ^ mn);  // n > R >= 1 unique keys: mx != mn
+    T = hb == 63 ? 0ull : mx & ~((2ull << hb) - 1ull);  // shared prefix, lower bits 0
+    for (int bit = hb; bit >= 0; --bit) {
+      const u64 cand = T | (1ull << bit);
+      int c = 0;
+#pragma unroll
+      for (int v = 0; v < Q; ++v) c += __popcll(__ballot(key[v] >= cand));
+      if (c >= R) {
+        T = cand;
+        if (c == R) break;
+      }
+    }
+  }
+  int base = 0;
+#pragma unroll
+  for (int v = 0; v < Q; ++v) {
+    const bool sel = key[v] >= T && key[v] != 0ull;
+    const u64 bs = __ballot(sel);
+    const int pos = base + __popcll(bs & lt);
+    if (sel && pos < R) out[pos] = key[v];  // exactly R keys qualify
+    base += __popcll(bs);
+  }
+}
+
+// The rank-pair candidates as registers (element c = v*64 + lane is the pair
+// (a, c - off[a]) with off[a] <= c < off[a+1]), then their top K into fs.
+// Always inlined: rs, cs and off must stay known LDS pointers.  Through a
+// generic pointer the compiler may fold the positive part of cs[c - off[a]]
+// into the instruction offset and leave a base below the LDS window, which
+// the hardware faults on.
+template <int Q>
+__device__ __attribute__((always_inline)) void select_cands_regs(const u64* rs, const u64* cs,
+                                                                 const int* off, int Kr, int P,
+                                                                 int Nc, int K, u64* fs) {
+  const int lane = threadIdx.x & 63;
+  u64 cand[Q];
+#pragma unroll
+  for (int v = 0; v < Q; ++v) {
+    const int c = v * 64 + lane;
+    cand[v] = 0ull;
+    if (c < P) {
+      int lo = 0, hi = Kr - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      const u64 rk = rs[lo], ck = cs[c - off[lo]];
+      cand[v] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
+    }
+  }
+  select_top_keys<Q>(cand, P, K, fs);
+}
+
 __device__ __forceinline__ u64 xor_lane64(u64 v, int j) {
   const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
   int a, b;
@@ -452,6 +542,7 @@ __device__ void emit_topk(const u64* fs, int K, int32_t* idx, float* score, floa
 
 struct TopkLayout {
   int Kr, Kc, P;
+  int regq;  // registers per lane holding the candidates, 0: candidates in LDS
   size_t o_rs, o_cs, o_cand, o_fs, o_hist, o_off, bytes;
 };
 
@@ -460,12 +551,18 @@ inline TopkLayout topk_layout(int Nr, int Nc, int K) {
   l.Kr = K < Nr ? K : Nr;
   l.Kc = K < Nc ? K : Nc;
   l.P = pair_count(K, l.Kr, l.Kc);
+  // register candidates only in the kernels for grid sides up to 24*64
+  // (their row values leave room for them)
+  const int q = (l.P + 63) / 64;
+  l.regq = (Nr > 24 * 64 || Nc > 24 * 64) ? 0
+         : q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : q <= 12 ? 12 : q <= 16 ? 16
+         : q <= 24 ? 24 : 0;
   size_t o = 0;
   l.o_rs = o; o += (size_t)l.Kr * 8;
   l.o_cs = o; o += (size_t)l.Kc * 8;
-  l.o_cand = o; o += (size_t)l.P * 8;
+  l.o_cand = o; o += l.regq ? 0 : (size_t)l.P * 8;
   l.o_fs = o; o += (size_t)K * 8;
-  l.o_hist = o; o += 256 * 4;
+  l.o_hist = o; o += l.regq ? 0 : 256 * 4;
   l.o_off = o; o += (size_t)(l.Kr + 1) * 4;
   l.bytes = (o + 15) & ~(size_t)15;  // slices of several tokens stay 16-byte aligned
   return l;
@@ -501,6 +598,9 @@ __device__ __forceinline__ void log_softmax_ord(const float* s, int n, unsigned 
 //     min(K_c, K/(a+1)) columns: a cell at ranks (a, b) has at least
 //     (a+1)(b+1) - 1 cells before it, so (a+1)(b+1) <= K is necessary.
 //  4. Top K of the candidates under (S desc, n asc); gate = softmax of S.
+//     At most 24*64 candidates (K up to about 270) are held in registers,
+//     24 per lane, which keeps the LDS slice of a token at 3K keys and lets
+//     five tokens share each SIMD; more are staged in LDS.
 // Several tokens share a workgroup (one wave each, each with its own LDS
 // slice): one-wave workgroups leave most wave slots of a CU empty.
 template <int VPL>
@@ -550,21 +650,32 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   }
   wave_sync();
 
-  // 3. candidate c belongs to the row rank a with off[a] <= c < off[a+1]
-  for (int c = lane; c < lay.P; c += 64) {
-    int lo = 0, hi = lay.Kr - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= c) lo = mid;
-      else hi = mid - 1;
+  // 3-4. candidate c belongs to the row rank a with off[a] <= c < off[a+1];
+  // their top K goes to fs.  Up to 24*64 candidates stay in registers
+  // (bit search by ballots); more are staged in LDS (radix select).
+  switch (VPL <= 24 ? lay.regq : 0) {
+    case 1: select_cands_regs<1>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 2: select_cands_regs<2>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 4: select_cands_regs<4>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 8: select_cands_regs<8>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 12: select_cands_regs<12>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 16: select_cands_regs<16>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 24: select_cands_regs<24>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    default: {
+      for (int c = lane; c < lay.P; c += 64) {
+        int lo = 0, hi = lay.Kr - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= c) lo = mid;
+          else hi = mid - 1;
+        }
+        const u64 rk = rs[lo], ck = cs[c - off[lo]];
+        cand[c] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
+      }
+      wave_sync();
+      select_top_lds(cand, lay.P, K, hist, fs);
     }
-    const u64 rk = rs[lo], ck = cs[c - off[lo]];
-    cand[c] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
   }
-  wave_sync();
-
-  // 4. top K of the candidates, ordered, gated and written
-  select_top_lds(cand, lay.P, K, hist, fs);
   wave_sync();
   int32_t* io = idx + (size_t)t * K;
   float* so = score + (size_t)t * K;
@@ -600,8 +711,10 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
                               float* score, float* gate, hipStream_t s) {
   const TopkLayout lay = topk_layout(Nr, Nc, K);
   const int need = (max(Nr, Nc) + 63) / 64;  // values per lane
-  // per token at most K*(3 + H(K)) keys: under 42 KB for K <= 512; up to
-  // four tokens share a workgroup within the default 64 KB of dynamic LDS
+  // per token 3K keys (rows, columns, the selected K) and the row offsets,
+  // plus the candidates (at most K*(1 + H(K)) keys) when they do not fit in
+  // registers: under 42 KB for K <= 512; up to four tokens share a
+  // workgroup within the default 64 KB of dynamic LDS
   const size_t lds = lay.bytes;
   const int wpg = lds * 4 <= 65536 ? 4 : lds * 2 <= 65536 ? 2 : 1;
 #define OMNI_TOPK(V)                                                                           \
