@@ -178,6 +178,37 @@ def test_token_ordered_output_pass(case):
         bo.y.fill_(7.0)
 
 
+TIE_CASES = [
+    (40, 50, 16, "bf16"),     # candidates in one register per lane
+    (8, 8, 20, "f32"),        # K > N_c: the top K spans three rows
+    (1304, 1304, 256, "bf16"),  # 24 candidate registers per lane
+    (600, 700, 512, "bf16"),  # more than 24*64 candidates: LDS select
+    (2900, 70, 256, "bf16"),  # grid side above 24*64: LDS select
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: "{}x{}_K{}_{}".format(*c))
+def test_exact_ties_take_the_smallest_ids(case):
+    """x = 0 makes every logit 0, so every cell scores -log N_r - log N_c:
+    under (S desc, n asc) the top K is n = 0 .. K-1 in that order, with
+    gates 1/K (a closed form, independent of the oracle)."""
+    Nr, Nc, K, dtype = case
+    L, d = 5, 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(3)
+    x = torch.zeros((L, d), dtype=tdt, device="cuda")
+    Wr = (torch.randn((Nr, d), generator=g) / d ** 0.5).to(tdt).cuda()
+    Wc = (torch.randn((Nc, d), generator=g) / d ** 0.5).to(tdt).cuda()
+    say(f"ties {case}")
+    idx, score, gate = omni.omni_router(x, Wr, Wc, K)
+    torch.cuda.synchronize()
+    want = torch.arange(K, dtype=torch.int32).expand(L, K)
+    assert torch.equal(idx.cpu(), want)
+    s_star = -float(np.log(Nr)) - float(np.log(Nc))
+    assert torch.allclose(score.cpu(), torch.full((L, K), s_star), atol=1e-5, rtol=0)
+    assert torch.allclose(gate.cpu(), torch.full((L, K), 1.0 / K), atol=1e-7, rtol=1e-5)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = synth.WORKLOADS[synth.TINY]
     inp = {k: v.cuda() for k, v in synth.make_inputs(w, seed=5).items()}
