@@ -150,7 +150,7 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
 size_t router_topk_lds_bytes(int Nr, int Nc, int K);
 
 struct SchedPlan {
-  int M, G, ntiles, passes, digit_bits;
+  int M, G, rounds, ntiles, passes, digit_bits;  // a tile is rounds x 256 elements
   size_t ws_bytes;
   // workspace carve (byte offsets)
   size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals;

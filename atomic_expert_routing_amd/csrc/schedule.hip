@@ -25,8 +25,12 @@ namespace omni {
 namespace {
 
 constexpr int SCHED_THREADS = 256;
-constexpr int SCHED_ROUNDS = 8;  // elements per tile = 256 * 8
-constexpr int SCHED_TILE = SCHED_THREADS * SCHED_ROUNDS;
+// A tile is `rounds` x 256 elements, rounds a power of two from 2 to 16:
+// the smallest that keeps the tile count at or below SCHED_MAX_TILES.  The
+// passes are latency bound; measured (one pass pair + offsets) at 2^19
+// elements 36 us with 1024 tiles against 42 us with 256, at 2^22 elements
+// 95 us with 1024 tiles against 100 us with 2048 and 122 us with 8192.
+constexpr int SCHED_MAX_TILES = 1024;
 
 // Element p's key: its group, idx[p * stride] / B, in the first pass; the
 // previous pass's sorted key afterwards.
@@ -39,14 +43,14 @@ __device__ __forceinline__ int load_key(const int32_t* __restrict__ idx,
 __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ keys_in,
                                                             int M, int stride, int B, int shift,
-                                                            int radix,
+                                                            int radix, int rounds,
                                                             int ntiles, int* __restrict__ hist) {
   __shared__ int h[256];
   const int tid = threadIdx.x, tile = blockIdx.x;
   if (tid < radix) h[tid] = 0;
   __syncthreads();
-  const int base = tile * SCHED_TILE;
-  for (int r = 0; r < SCHED_ROUNDS; ++r) {
+  const int base = tile * rounds * SCHED_THREADS;
+  for (int r = 0; r < rounds; ++r) {
     const int p = base + r * SCHED_THREADS + tid;
     if (p < M) atomicAdd(&h[(load_key(idx, keys_in, p, stride, B) >> shift) & (radix - 1)], 1);
   }
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(int* __restri
 __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
     const int32_t* __restrict__ vals_in, int M, int stride, int B, int shift, int radix,
-    int ntiles,
+    int rounds, int ntiles,
     const int* __restrict__ hist, const int* __restrict__ totals, int32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out) {
   __shared__ int run[256];
@@ -126,8 +130,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
   if (tid < radix) run[tid] += hist[(size_t)tid * ntiles + tile];
   __syncthreads();
   const unsigned long long lt = (1ull << lane) - 1ull;
-  const int base = tile * SCHED_TILE;
-  for (int r = 0; r < SCHED_ROUNDS; ++r) {
+  const int base = tile * rounds * SCHED_THREADS;
+  for (int r = 0; r < rounds; ++r) {
     const int p = base + r * SCHED_THREADS + tid;
     const bool act = p < M;
     int key = 0, val = 0, dig = 0;
@@ -189,7 +193,11 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B) {
   while (bits < 31 && (1ll << bits) < p.G) ++bits;  // groups 0 .. G-1 fit in `bits`
   p.passes = (bits + 7) / 8;
   p.digit_bits = (bits + p.passes - 1) / p.passes;
-  p.ntiles = (p.M + SCHED_TILE - 1) / SCHED_TILE;
+  p.rounds = 2;
+  while (p.rounds < 16 && ((int64_t)p.M + SCHED_THREADS * p.rounds - 1) / (SCHED_THREADS * p.rounds) >
+                              SCHED_MAX_TILES)
+    p.rounds *= 2;
+  p.ntiles = (p.M + SCHED_THREADS * p.rounds - 1) / (SCHED_THREADS * p.rounds);
   const size_t arr = align256((size_t)p.M * 4);
   p.off_keys_a = 0;
   p.off_vals_a = arr;
@@ -229,11 +237,12 @@ void sort_by_group(const int32_t* idx, int stride, int M, int B, const SchedPlan
     int32_t* vout = last ? vals_last : ((pass & 1) ? vb : va);
     const int shift = pass * plan.digit_bits;
     hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M,
-                       stride, B, shift, radix, plan.ntiles, hist);
+                       stride, B, shift, radix, plan.rounds, plan.ntiles, hist);
     hipLaunchKernelGGL(sched_scan_digits, dim3(radix), dim3(SCHED_THREADS), 0, s, hist,
                        plan.ntiles, totals);
     hipLaunchKernelGGL(sched_scatter, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, vin,
-                       M, stride, B, shift, radix, plan.ntiles, hist, totals, kout, vout);
+                       M, stride, B, shift, radix, plan.rounds, plan.ntiles, hist, totals, kout,
+                       vout);
     kin = kout;
     vin = vout;
   }
