@@ -368,12 +368,12 @@ __device__ __forceinline__ u64 wave_umin64(u64 v) {
 }
 
 // Select the R largest of n unique nonzero 64-bit keys held in registers
-// (key[v] of a lane is element v*64 + lane; 0 pads the slots past n).  The
+// (Q per lane, in any arrangement; 0 pads the unused slots).  The
 // R-th largest key T is found bit by bit below the leading bits all keys
 // share, keeping count(>= T) >= R and stopping as soon as exactly R keys
 // qualify; being unique, exactly R keys are >= the final T.  They are
-// written to out[0..R) in element order.  Always inlined so that `out`
-// stays a known LDS pointer (DS instructions, no generic addressing).
+// written to out[0..R) (in slot order v, then lane).  Always inlined so that
+// `out` stays a known LDS pointer (DS instructions, no generic addressing).
 template <int Q>
 __device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[Q], int n, int R,
                                                                u64* out) {
@@ -385,7 +385,7 @@ __device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[
 #pragma unroll
     for (int v = 0; v < Q; ++v) {
       mx = key[v] > mx ? key[v] : mx;
-      const u64 k = v * 64 + lane < n ? key[v] : ~0ull;
+      const u64 k = key[v] != 0ull ? key[v] : ~0ull;  // 0 pads
       mn = k < mn ? k : mn;
     }
     mx = wave_umax64(mx);
@@ -414,30 +414,56 @@ __device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[
   }
 }
 
-// The rank-pair candidates as registers (element c = v*64 + lane is the pair
-// (a, c - off[a]) with off[a] <= c < off[a+1]), then their top K into fs.
-// Always inlined: rs, cs and off must stay known LDS pointers.  Through a
-// generic pointer the compiler may fold the positive part of cs[c - off[a]]
-// into the instruction offset and leave a base below the LDS window, which
-// the hardware faults on.
+// The rank-pair candidates as registers, then their top K into fs.  Lane l
+// holds candidates c = l*Q .. l*Q + Q-1 (a contiguous run of the row-major
+// rank-pair order): one binary search over the row offsets finds the row of
+// its first candidate, and the run advances through the rows by arithmetic
+// (row a has min(K_c, floor(K/(a+1))) candidates, at least one), so only
+// the row and column keys are read from LDS.  Always inlined: rs, cs and
+// off must stay known LDS pointers.  Through a generic pointer the compiler
+// may fold a constant part of an index into the instruction offset and
+// leave a base below the LDS window, which the hardware faults on.
 template <int Q>
 __device__ __attribute__((always_inline)) void select_cands_regs(const u64* rs, const u64* cs,
                                                                  const int* off, int Kr, int P,
-                                                                 int Nc, int K, u64* fs) {
+                                                                 int Kc, int Nc, int K, u64* fs) {
   const int lane = threadIdx.x & 63;
+  const int c0 = lane * Q;
+  int a = 0;
+  if (c0 < P) {
+    int hi = Kr - 1;
+    while (a < hi) {
+      const int mid = (a + hi + 1) >> 1;
+      if (off[mid] <= c0) a = mid;
+      else hi = mid - 1;
+    }
+  }
+  int cur = c0 < P ? off[a] : 0;  // first candidate of row a
+  auto row_count = [&](int r) {   // min(K_c, floor(K / (r + 1))), exact for K < 2^20
+    int q = (int)((float)K * __builtin_amdgcn_rcpf((float)(r + 1)));
+    q += (q + 1) * (r + 1) <= K;
+    q -= q * (r + 1) > K;
+    return min(Kc, q);
+  };
+  int nxt = cur + row_count(a);
+  int ra[Q], cb[Q];
+#pragma unroll
+  for (int v = 0; v < Q; ++v) {
+    const int c = c0 + v;
+    if (c == nxt && c < P) {  // rows hold at least one candidate: one step at a time
+      ++a;
+      cur = nxt;
+      nxt += row_count(a);
+    }
+    ra[v] = a;
+    cb[v] = c - cur;
+  }
   u64 cand[Q];
 #pragma unroll
   for (int v = 0; v < Q; ++v) {
-    const int c = v * 64 + lane;
     cand[v] = 0ull;
-    if (c < P) {
-      int lo = 0, hi = Kr - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= c) lo = mid;
-        else hi = mid - 1;
-      }
-      const u64 rk = rs[lo], ck = cs[c - off[lo]];
+    if (c0 + v < P) {
+      const u64 rk = rs[ra[v]], ck = cs[cb[v]];
       cand[v] = make_key(key_val(rk) + key_val(ck), key_idx(rk) * (unsigned)Nc + key_idx(ck));
     }
   }
@@ -654,13 +680,13 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   // their top K goes to fs.  Up to 24*64 candidates stay in registers
   // (bit search by ballots); more are staged in LDS (radix select).
   switch (VPL <= 24 ? lay.regq : 0) {
-    case 1: select_cands_regs<1>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 2: select_cands_regs<2>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 4: select_cands_regs<4>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 8: select_cands_regs<8>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 12: select_cands_regs<12>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 16: select_cands_regs<16>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
-    case 24: select_cands_regs<24>(rs, cs, off, lay.Kr, lay.P, Nc, K, fs); break;
+    case 1: select_cands_regs<1>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 2: select_cands_regs<2>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 4: select_cands_regs<4>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 8: select_cands_regs<8>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 12: select_cands_regs<12>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 16: select_cands_regs<16>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
+    case 24: select_cands_regs<24>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs); break;
     default: {
       for (int c = lane; c < lay.P; c += 64) {
         int lo = 0, hi = lay.Kr - 1;
