@@ -159,7 +159,7 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
                                                   int ucap, int32_t* __restrict__ U,
                                                   int32_t* __restrict__ nU, float* __restrict__ G,
                                                   int32_t* __restrict__ kmap) {
-  extern __shared__ int keys[];
+  extern __shared__ __attribute__((aligned(16))) int keys[];
   __shared__ int wtot[16];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int nt = BT * K;
@@ -221,10 +221,18 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
   for (int c = tid; c < npad; c += 1024) Ub[c] = n ? keys[min(c, n - 1)] : 0;
   if (tid == 0) nU[b] = n;
   // the gate tile G_b [64][npad]: every entry marked "no task", then each
-  // task's gate at (its row, its id's position in the union)
+  // task's gate at (its row, its id's position in the union).  With room
+  // for 8 or more tile rows in the LDS of the sort, the rows are assembled
+  // there and stored whole; otherwise the tile is filled in place and the
+  // gates are stored one by one (4-byte stores to scattered lines).
   uint32_t* Gb = (uint32_t*)G + (size_t)b * BT * ucap;
-  const int n4 = BT * npad / 4;
-  for (int i = tid; i < n4; i += 1024) ((u32x4*)Gb)[i] = u32x4{NOTASK, NOTASK, NOTASK, NOTASK};
+  constexpr int LDS_WORDS = 1024 * E + 1024;
+  const int rows_per_pass = min(BT, LDS_WORDS / npad);
+  const bool staged = KEEP && kmap == nullptr && rows_per_pass >= 8;
+  if (!staged) {
+    const int n4 = BT * npad / 4;
+    for (int i = tid; i < n4; i += 1024) ((u32x4*)Gb)[i] = u32x4{NOTASK, NOTASK, NOTASK, NOTASK};
+  }
   __syncthreads();  // the fill is complete before the gates land on it
   auto position = [&](int e) {  // e is in the union: its index there
     int lo = 0, hi = n - 1;
@@ -246,6 +254,27 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
 #pragma unroll
       for (int q = 0; q < E; ++q) base[q] += keys[base[q] + half] < id0[q] ? half : 0;
       len -= half;
+    }
+    if (staged) {
+      int col[E];
+#pragma unroll
+      for (int q = 0; q < E; ++q) col[q] = base[q] + (keys[base[q]] < id0[q]);
+      uint32_t* stage = (uint32_t*)keys;
+      for (int r0 = 0; r0 < BT; r0 += rows_per_pass) {
+        const int rows = min(rows_per_pass, BT - r0);
+        __syncthreads();  // the union searches, or the previous pass's stores, are done
+        for (int i = tid; i < rows * npad; i += 1024) stage[i] = NOTASK;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          const int r = (tid * E + q) / K - r0;
+          if (id0[q] != INT_MAX && r >= 0 && r < rows) stage[r * npad + col[q]] = __float_as_uint(g0[q]);
+        }
+        __syncthreads();
+        u32x4* dst = (u32x4*)(Gb + (size_t)r0 * npad);
+        for (int i = tid; i < rows * npad / 4; i += 1024) dst[i] = ((const u32x4*)stage)[i];
+      }
+      return;
     }
 #pragma unroll
     for (int q = 0; q < E; ++q) {
