@@ -260,9 +260,9 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_write(const int32_t* __restri
 // slower, 1.96 ms against 1.70 ms: a wave's row stores then sit between its
 // loads, and gfx9's single vector-memory counter makes the loads wait for
 // them.)
-// bf16 rows are stored non-temporally (the x and dy rows the next segments
-// read stay in L2: 2.10 -> 1.93 ms at 4096 tokens x 1.7M experts); for fp32
-// rows the same hint was much slower (2.6 -> 4.0 ms) and is not used.
+// The rows are stored non-temporally, so that the x and dy rows the next
+// segments read stay in L2 (bf16 rows: whole call 2.10 -> 1.93 ms at 4096
+// tokens x 1.7M experts).
 template <bool OUT_BF16, int E>
 __device__ __forceinline__ void store_row_chunk(void* rows, size_t r, int d, int c,
                                                 const float* v) {
@@ -281,6 +281,26 @@ __device__ __forceinline__ void store_row_chunk(void* rows, size_t r, int d, int
       const int q = E - 4;
       uint2 w{bf16_rne(v[q]) | (bf16_rne(v[q + 1]) << 16), bf16_rne(v[q + 2]) | (bf16_rne(v[q + 3]) << 16)};
       *(uint2*)(o + q) = w;
+    }
+  } else if (E == 8 && d % 512 == 0) {
+    // fp32 rows from bf16 inputs: a wave's 64 chunks are 2 KB of the row.
+    // Lanes exchange halves so that each of the two stores writes 1 KB
+    // contiguously (lane l: floats 4l.. of the wave's first or second KB),
+    // then store non-temporally; without the exchange a store instruction
+    // covers every other 16 bytes, and non-temporal stores of such half
+    // lines made the call 1.5x slower.
+    const int lane = threadIdx.x & 63;
+    float* o = (float*)rows + r * d + (c - lane) * E;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int src = 32 * half + (lane >> 1);
+      f32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __shfl(v[i], src, 64), hi = __shfl(v[4 + i], src, 64);
+        w[i] = (lane & 1) ? hi : lo;
+      }
+      __builtin_nontemporal_store(w, (f32x4*)(o + 256 * half + 4 * lane));
     }
   } else {
     float* o = (float*)rows + r * d + c * E;
