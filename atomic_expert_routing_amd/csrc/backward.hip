@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void expert_bwd_token(
     for (int j = 0; j < NCH; ++j) {
       const int c = lane + 64 * j;
       const bool in = live && c < nchunk;
-      w[j] = in ? *(const u32x4*)(wb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
-      v[j] = in ? *(const u32x4*)(vb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
+      w[j] = in ? __builtin_nontemporal_load((const u32x4*)(wb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
+      v[j] = in ? __builtin_nontemporal_load((const u32x4*)(vb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto task = [&](int k, const u32x4* w, const u32x4* v) {
