@@ -12,6 +12,10 @@ arithmetic).  Prints ONE JSON line.
 Timing: W untimed steps, then exactly K steps between two device
 synchronisations (wall clock), with HIP events (torch.cuda.Event on the
 stream the library launches on) around each call for the per-stage split.
+Then a second branch on a second stream runs alternate steps (two batches
+in flight, each step the whole path on its own buffers), reported as
+two_stream_ms_per_step: one step's router and schedule overlap the other's
+assembly.  It is a throughput figure beside the value, not the value.
 Then the same step is captured once as a HIP graph (the three calls'
 kernels, on preallocated buffers) and W + K replays are timed the same way
 (graph_ms_per_step; --graph makes it the value).  Measured on MI355X the
@@ -398,6 +402,7 @@ def main():
     from atomic_expert_routing_amd import omni, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pipe_streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
     w = synth.WORKLOADS[args.workload or synth.HEADLINE]
     log(f"[bench] workload {w.name}: generating inputs on the GPU")
     inp = synth.make_inputs(w, seed=args.seed, device="cuda")
@@ -442,6 +447,38 @@ def main():
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_step = eager_ms
+    # two batches in flight: a second branch (own outputs and workspace) on a
+    # second stream, steps alternating between the two; each step does the
+    # whole path, and the two streams overlap one step's router and schedule
+    # with the other's assembly.  Timed before any graph capture: after one,
+    # launches on the two streams were measured to no longer overlap.
+    br2 = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype,
+                            token_order=args.token_order, assembly=args.assembly)
+    pair = [(br, pipe_streams[0]), (br2, pipe_streams[1])]
+
+    def two_stream(n):
+        start = torch.cuda.Event()
+        start.record(torch.cuda.current_stream())
+        for _, st in pair:
+            st.wait_event(start)
+        for i in range(n):
+            b, st = pair[i % 2]
+            with torch.cuda.stream(st):
+                b.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+        for _, st in pair:
+            done = torch.cuda.Event()
+            done.record(st)
+            torch.cuda.current_stream().wait_event(done)
+
+    two_stream(args.warmup + 1)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps on two streams")
+    t0 = time.perf_counter()
+    two_stream(args.steps)
+    torch.cuda.synchronize()
+    two_stream_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    two_stream_same_y = bool(torch.equal(br.y, br2.y))
+    del br2, pair
     # the same step captured once as a HIP graph and replayed
     br.capture(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     for _ in range(args.warmup):
@@ -495,6 +532,10 @@ def main():
                   else "eager launches",
         "eager_ms_per_step": round(eager_ms, 4),
         "graph_ms_per_step": round(graph_ms, 4),
+        "two_stream_ms_per_step": round(two_stream_ms, 4),
+        "two_stream_note": "throughput with two independent batches in flight on two streams "
+                           "(each step the whole path on its own buffers); not the value",
+        "two_stream_y_bitwise_equal": two_stream_same_y,
         "branch_hbm_frac": round(branch_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "stages_ms_median": {"router": round(router_ms, 4), "schedule": round(sched_ms, 4),
                              "expert_forward": round(expert_ms, 4),
