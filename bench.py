@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--assembly", choices=("expert_centric", "blocked"), default="expert_centric",
                     help="assembly of the headline step (blocked: dense products per token "
                          "block, for clustered routing)")
+    ap.add_argument("--no-two-stream", action="store_true",
+                    help="skip the two-batch, two-stream throughput measurement (profiling runs "
+                         "use it so that kernel durations are not measured while two steps "
+                         "share the GPU)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward calls")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -470,14 +474,16 @@ def main():
             done.record(st)
             torch.cuda.current_stream().wait_event(done)
 
-    two_stream(args.warmup + 1)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps on two streams")
-    t0 = time.perf_counter()
-    two_stream(args.steps)
-    torch.cuda.synchronize()
-    two_stream_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    two_stream_same_y = bool(torch.equal(br.y, br2.y))
+    two_stream_ms, two_stream_same_y = None, None
+    if not args.no_two_stream:
+        two_stream(args.warmup + 1)
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} steps on two streams")
+        t0 = time.perf_counter()
+        two_stream(args.steps)
+        torch.cuda.synchronize()
+        two_stream_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        two_stream_same_y = bool(torch.equal(br.y, br2.y))
     del br2, pair
     # the same step captured once as a HIP graph and replayed
     br.capture(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
@@ -532,7 +538,7 @@ def main():
                   else "eager launches",
         "eager_ms_per_step": round(eager_ms, 4),
         "graph_ms_per_step": round(graph_ms, 4),
-        "two_stream_ms_per_step": round(two_stream_ms, 4),
+        "two_stream_ms_per_step": None if two_stream_ms is None else round(two_stream_ms, 4),
         "two_stream_note": "throughput with two independent batches in flight on two streams "
                            "(each step the whole path on its own buffers); not the value",
         "two_stream_y_bitwise_equal": two_stream_same_y,
