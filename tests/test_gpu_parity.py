@@ -106,6 +106,29 @@ def test_schedule_on_oracle_routing_is_bit_exact():
         check_schedule(idx_o, perm, off, w.N, B)
 
 
+SCHED_SIZES = [
+    (3000, 100, 50000, 7, None),          # 300,000 tasks, 2 x 256 per tile, ragged tail
+    (8192, 128, 1700416, 128, None),      # 2^20 tasks: 4 x 256 per tile
+    (16384, 128, 280900, 64, None),       # 2^21 tasks: 8 x 256 per tile
+    (16384, 200, 1048576, 128, None),     # 3,276,800 tasks: 16 x 256 per tile, ragged
+    (16384, 128, 1700416, 128, 3000),     # 2^21 tasks on 3000 experts: few, crowded groups
+]
+
+
+@pytest.mark.parametrize("case", SCHED_SIZES, ids=lambda c: "L{}_K{}_N{}_B{}_ids{}".format(*c))
+def test_schedule_tile_sizes_are_bit_exact(case):
+    """The radix passes size their tiles by the task count (2 to 16 rounds of
+    256 tasks); perm and group_off must match the oracle bit for bit at each."""
+    L, K, N, B, span = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    idx_np = rng.integers(0, span or N, size=(L, K), dtype=np.int64)
+    say(f"schedule sizes {case}")
+    idx = torch.as_tensor(idx_np, dtype=torch.int32, device="cuda")
+    perm, off = omni.omni_schedule(idx, N, B)
+    torch.cuda.synchronize()
+    check_schedule(idx_np, perm, off, N, B)
+
+
 def test_expert_forward_on_oracle_routing():
     w = synth.WORKLOADS[synth.TINY]
     inp = synth.make_inputs(w, seed=4)
