@@ -397,7 +397,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the routed "
-              "branch here is a single-GPU kernel path; see the sharding notes in DESIGN.md",
+              "branch here is a single-GPU kernel path (it would shard by token or by ranges of "
+              "expert groups, with an all-gather of ids and x and a reduce-scatter of y)",
               file=sys.stderr)
         sys.exit(2)
 
