@@ -221,14 +221,18 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
   for (int c = tid; c < npad; c += 1024) Ub[c] = n ? keys[min(c, n - 1)] : 0;
   if (tid == 0) nU[b] = n;
   // the gate tile G_b [64][npad]: every entry marked "no task", then each
-  // task's gate at (its row, its id's position in the union).  With room
-  // for 8 or more tile rows in the LDS of the sort, the rows are assembled
-  // there and stored whole; otherwise the tile is filled in place and the
-  // gates are stored one by one (4-byte stores to scattered lines).
+  // task's gate at (its row, its id's position in the union); the slot map
+  // (when asked for) holds each task's k at the same place and is read only
+  // where the gate tile holds a task.  With room for 8 or more tile rows
+  // (of both) in the LDS of the sort, the rows are assembled there and
+  // stored whole; otherwise the gate tile is filled in place and the entries
+  // are stored one by one (4-byte stores to scattered lines).
   uint32_t* Gb = (uint32_t*)G + (size_t)b * BT * ucap;
+  int32_t* Kb = kmap ? kmap + (size_t)b * BT * ucap : nullptr;
   constexpr int LDS_WORDS = 1024 * E + 1024;
-  const int rows_per_pass = min(BT, LDS_WORDS / npad);
-  const bool staged = KEEP && kmap == nullptr && rows_per_pass >= 8;
+  const int row_words = kmap ? 2 * npad : npad;
+  const int rows_per_pass = min(BT, LDS_WORDS / row_words);
+  const bool staged = KEEP && rows_per_pass >= 8;
   if (!staged) {
     const int n4 = BT * npad / 4;
     for (int i = tid; i < n4; i += 1024) ((u32x4*)Gb)[i] = u32x4{NOTASK, NOTASK, NOTASK, NOTASK};
@@ -259,20 +263,31 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
       int col[E];
 #pragma unroll
       for (int q = 0; q < E; ++q) col[q] = base[q] + (keys[base[q]] < id0[q]);
-      uint32_t* stage = (uint32_t*)keys;
+      uint32_t* stage = (uint32_t*)keys;                 // gate rows
+      uint32_t* kstage = stage + rows_per_pass * npad;   // slot rows (with kmap)
       for (int r0 = 0; r0 < BT; r0 += rows_per_pass) {
         const int rows = min(rows_per_pass, BT - r0);
         __syncthreads();  // the union searches, or the previous pass's stores, are done
-        for (int i = tid; i < rows * npad; i += 1024) stage[i] = NOTASK;
+        for (int i = tid; i < rows * npad; i += 1024) {
+          stage[i] = NOTASK;
+          if (kmap) kstage[i] = 0u;
+        }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < E; ++q) {
-          const int r = (tid * E + q) / K - r0;
-          if (id0[q] != INT_MAX && r >= 0 && r < rows) stage[r * npad + col[q]] = __float_as_uint(g0[q]);
+          const int i = tid * E + q, r = i / K;
+          if (id0[q] != INT_MAX && r >= r0 && r < r0 + rows) {
+            stage[(r - r0) * npad + col[q]] = __float_as_uint(g0[q]);
+            if (kmap) kstage[(r - r0) * npad + col[q]] = (uint32_t)(i - r * K);
+          }
         }
         __syncthreads();
         u32x4* dst = (u32x4*)(Gb + (size_t)r0 * npad);
         for (int i = tid; i < rows * npad / 4; i += 1024) dst[i] = ((const u32x4*)stage)[i];
+        if (kmap) {
+          u32x4* kdst = (u32x4*)(Kb + (size_t)r0 * npad);
+          for (int i = tid; i < rows * npad / 4; i += 1024) kdst[i] = ((const u32x4*)kstage)[i];
+        }
       }
       return;
     }

@@ -223,12 +223,12 @@ BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K);
 // seg[n_uniq] = L*K)
 hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int32_t* n_uniq,
                                   const BwdPlan& p, void* ws, hipStream_t s);
-// used experts and their dW / dV rows from the per-task terms dh, ga that
-// the plan's workspace already holds (the second half of the backward)
-hipError_t launch_expert_grad_rows(const void* x, const float* dy, const int32_t* idx, int L, int d,
-                                   int N, int K, omni_dtype dt, int32_t* uniq, int32_t* n_uniq,
-                                   omni_dtype grad_dt, void* dW_rows, void* dV_rows,
-                                   const BwdPlan& p, void* ws, hipStream_t s);
+// the used experts' dW / dV rows from the per-task terms dh, ga and the
+// sort by expert (launch_expert_segments) that the plan's workspace already
+// holds (the last step of the backward)
+hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K, omni_dtype dt,
+                                   const int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
+                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s);
 // dx (expert part, overwritten), dgate, used experts and their dW / dV rows
 hipError_t launch_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
                                   const float* gate, const float* dy, int L, int d, int N, int K,
