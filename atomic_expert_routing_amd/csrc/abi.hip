@@ -91,6 +91,8 @@ omni_status expert_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt,
 omni_status expert_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
   omni_status s;
   if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
+  if (L > I32_LIMIT - 8)  // the row pass keys tokens by 8 * ceil(L / 8) + 1 values
+    return fail(OMNI_ERR_UNSUPPORTED, "L = %lld exceeds 2^31-9", (long long)L);
   *out = omni::plan_expert_backward(L, d, N, K).ws_bytes;
   return OMNI_OK;
 }

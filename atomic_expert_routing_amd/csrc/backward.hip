@@ -20,6 +20,11 @@
 //                      segments: list of used experts and segment starts.
 //   expert_bwd_token   one workgroup per token: its K (W, V) rows give h and u;
 //                      dgate, dh, ga per task and the token-owned dx_t.
+//   row_keys, a radix sort, row_recs
+//                      the used experts ordered for the row pass: by the
+//                      XCD class t % 8 of their first task's token t, then
+//                      by t, dealt out so that workgroup b (on XCD b % 8)
+//                      mostly takes an expert of class b % 8.
 //   expert_bwd_rows    one workgroup per used expert: dW and dV rows summed
 //                      over the expert's tasks in (token, k) order, written
 //                      once, no atomics (each row has one owner).
@@ -29,6 +34,8 @@
 //   transpose_bf16 + the MFMA product of the forward router (bf16 ds split
 //                      into a high and a low bf16 part, fp32 accumulation),
 //                      or gemm_f32_strided for fp32 inputs.
+
+#include <algorithm>
 
 #include "omni_internal.h"
 
@@ -267,6 +274,69 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_write(const int32_t* __restri
   }
 }
 
+// ------------------------------------------------------------------ the row order
+// The row pass reads, per task, the x and dy rows of the task's token; most
+// used experts have one task.  Workgroup b runs on XCD b % 8, whose L2 is its
+// own, so the used experts are dealt out by the token t of their first task:
+// class t % 8 goes to XCD t % 8, which then reads the x and dy rows of one
+// eighth of the tokens, and inside a class by ascending t, so that the
+// experts of one token run close together in time.
+//
+// key[u] = (t % 8) * Lq + t / 8 for used expert u (Lq = ceil(L / 8)), 8 * Lq
+// for the slots past n_uniq.
+__global__ __launch_bounds__(256) void row_keys(const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ seg,
+                                                const int32_t* __restrict__ n_uniq, int K, int Lq,
+                                                int U, int32_t* __restrict__ key) {
+  const int n = *n_uniq;
+  for (int u = blockIdx.x * 256 + threadIdx.x; u < U; u += gridDim.x * 256) {
+    int k = 8 * Lq;
+    if (u < n) {
+      const int t = perm[seg[u]] / K;
+      k = (t & 7) * Lq + (t >> 3);
+    }
+    key[u] = k;
+  }
+}
+
+// With rord = the used experts sorted by key and goff its key offsets, class
+// x is rord[goff[x Lq] .. goff[(x+1) Lq]).  With m the smallest class size,
+// workgroup b < 8m takes entry b / 8 of class b % 8; the classes' remaining
+// entries follow, class by class, from b = 8m.  rec[b] = {u, seg[u],
+// seg[u + 1], perm[seg[u]]}: the row, its task range and its first task, so
+// that the row pass starts its data loads at once.
+__global__ __launch_bounds__(256) void row_recs(const int32_t* __restrict__ rord,
+                                                const int32_t* __restrict__ goff,
+                                                const int32_t* __restrict__ seg,
+                                                const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ n_uniq, int Lq,
+                                                int4* __restrict__ rec) {
+  __shared__ int off[9];
+  if (threadIdx.x < 9) off[threadIdx.x] = goff[threadIdx.x * Lq];
+  __syncthreads();
+  const int n = *n_uniq;
+  int m = n;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) m = min(m, off[x + 1] - off[x]);
+  for (int b = blockIdx.x * 256 + threadIdx.x; b < n; b += gridDim.x * 256) {
+    int q;
+    if (b < 8 * m) {
+      q = off[b & 7] + (b >> 3);
+    } else {
+      int k = b - 8 * m, x = 0;
+      for (; x < 7; ++x) {  // the extras of classes 0..x-1 come first
+        const int extra = off[x + 1] - off[x] - m;
+        if (k < extra) break;
+        k -= extra;
+      }
+      q = off[x] + m + k;
+    }
+    const int u = rord[q];
+    const int s0 = seg[u];
+    rec[b] = int4{u, s0, seg[u + 1], perm[s0]};
+  }
+}
+
 // ------------------------------------------------------------------ expert_bwd_rows
 // One workgroup per used expert r (row uniq[r]); thread i owns 16 bytes of
 // the input row (E columns) of both gradients.  The segment's tasks are
@@ -330,14 +400,18 @@ __device__ __forceinline__ void store_row_chunk(void* rows, size_t r, int d, int
 template <bool BF16, bool OUT_BF16>
 __global__ __launch_bounds__(512) void expert_bwd_rows(
     const uint16_t* __restrict__ x_, const float* __restrict__ dy, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ seg_start, const int32_t* __restrict__ n_uniq,
+    const int4* __restrict__ rec, const int32_t* __restrict__ n_uniq,
     const float* __restrict__ dh, const float* __restrict__ ga, int d, int K,
     void* __restrict__ dW_rows, void* __restrict__ dV_rows) {
   using C = Chunk<BF16>;
   constexpr int E = C::E;
-  const int r = blockIdx.x;
-  if (r >= n_uniq[0]) return;
-  const int s0 = seg_start[r], s1 = seg_start[r + 1];
+  const int b = blockIdx.x;
+  // rec has a slot for every workgroup (the grid is the used-expert bound):
+  // both loads are issued together, and slots past n_uniq are never used
+  const int n = n_uniq[0];
+  const int4 rc = rec[b];
+  if (b >= n) return;
+  const int r = uni(rc.x), s0 = uni(rc.y), s1 = uni(rc.z), m0 = uni(rc.w);
   const int c = threadIdx.x;
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   if (c * 16u >= row_bytes) return;  // no barrier below
@@ -345,7 +419,7 @@ __global__ __launch_bounds__(512) void expert_bwd_rows(
 #pragma unroll
   for (int q = 0; q < E; ++q) aw[q] = av[q] = 0.f;
   auto load = [&](int p, u32x4& xv, f32x4* dv, float& sdh, float& sga) {
-    const int m = uni(perm[p]);
+    const int m = p == s0 ? m0 : uni(perm[p]);
     const int t = m / K;
     sdh = uni(dh[m]);
     sga = uni(ga[m]);
@@ -513,7 +587,15 @@ BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K) {
   p.off_eoff = take((size_t)(N + 1) * 4);
   p.off_seg = take((size_t)(p.M + 1) * 4);
   p.off_cnt = take((size_t)p.ntiles * 4);
-  p.off_sched = take(p.sched.ws_bytes);
+  // the row order: keys, the sorted experts, key offsets, one record per row
+  p.Lq = (int)((L + 7) / 8);
+  p.rsort = plan_schedule(p.U_max, 1, 8ll * p.Lq + 1, 1);
+  p.off_rkey = take((size_t)p.U_max * 4);
+  p.off_rord = take((size_t)p.U_max * 4);
+  p.off_goff = take((size_t)(8 * p.Lq + 2) * 4);
+  p.off_rec = take((size_t)p.U_max * 16);
+  // the expert sort's workspace is free again when the row order is sorted
+  p.off_sched = take(std::max(p.sched.ws_bytes, p.rsort.ws_bytes));
   p.ws_bytes = o;
   (void)d;
   return p;
@@ -563,6 +645,18 @@ hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K,
   float* ga = (float*)(w + p.off_ga);
   const int32_t* perm = (const int32_t*)(w + p.off_perm);
   const int32_t* seg = (const int32_t*)(w + p.off_seg);
+  int32_t* rkey = (int32_t*)(w + p.off_rkey);
+  int32_t* rord = (int32_t*)(w + p.off_rord);
+  int32_t* goff = (int32_t*)(w + p.off_goff);
+  int4* rec = (int4*)(w + p.off_rec);
+  const unsigned ogrid = (unsigned)std::min(2048, (p.U_max + 255) / 256);
+  hipLaunchKernelGGL(row_keys, dim3(ogrid), dim3(256), 0, s, perm, seg, n_uniq, K, p.Lq, p.U_max,
+                     rkey);
+  hipError_t e = launch_schedule(rkey, p.U_max, 1, 8 * p.Lq + 1, p.rsort, rord, goff,
+                                 w + p.off_sched, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_recs, dim3(ogrid), dim3(256), 0, s, rord, goff, seg, perm, n_uniq, p.Lq,
+                     rec);
   const bool bf = dt == OMNI_BF16;
   const int E = bf ? 8 : 4;
   const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
@@ -570,7 +664,7 @@ hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K,
   const bool obf = grad_dt == OMNI_BF16;
 #define OMNI_ROWS(IB, OB)                                                                        \
   hipLaunchKernelGGL((expert_bwd_rows<IB, OB>), grid, dim3(threads), 0, s, (const uint16_t*)x, dy, \
-                     perm, seg, n_uniq, dh, ga, d, K, dW_rows, dV_rows)
+                     perm, rec, n_uniq, dh, ga, d, K, dW_rows, dV_rows)
   if (bf && obf) OMNI_ROWS(true, true);
   else if (bf) OMNI_ROWS(true, false);
   else if (obf) OMNI_ROWS(false, true);

@@ -213,9 +213,10 @@ hipError_t launch_dense_router(const void* x, const void* Wn, int L, int d, int 
 
 // ----------------------------------------------------------------- backward
 struct BwdPlan {
-  int M, U_max, ntiles;
-  SchedPlan sched;
+  int M, U_max, ntiles, Lq;
+  SchedPlan sched, rsort;  // the sort of the tasks by expert; of the used experts for the rows
   size_t off_dh, off_ga, off_perm, off_eoff, off_seg, off_cnt, off_sched, ws_bytes;
+  size_t off_rkey, off_rord, off_goff, off_rec;
 };
 BwdPlan plan_expert_backward(int64_t L, int64_t d, int64_t N, int64_t K);
 // the tasks sorted by expert (the plan's perm), the used experts (uniq,

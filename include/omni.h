@@ -262,9 +262,11 @@ OMNI_API omni_status omni_expert_forward_token_centric(const void* x, const void
  * gradient: dense fp32 dW and dV would be 2*N*d*4 bytes).  Each row is summed
  * by one workgroup over the expert's tasks in (token, k) order, so the
  * result is deterministic.  Writing the rows is most of this call's memory
- * traffic; bf16 rows halve it.  Same size limits as omni_expert_forward.
- * Workspace: per-task terms, the tasks sorted by expert id and the
- * per-expert segment table (omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD)).
+ * traffic; bf16 rows halve it.  Same size limits as omni_expert_forward,
+ * and L <= 2^31-9 (OMNI_ERR_UNSUPPORTED above).
+ * Workspace: per-task terms, the tasks sorted by expert id, the per-expert
+ * segment table and the order in which the rows are summed
+ * (omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD)).
  */
 OMNI_API omni_status omni_expert_backward(const void* x, const void* W, const void* V,
                                           const int32_t* idx, const float* gate, const float* dy,

@@ -134,11 +134,13 @@ def test_calls_reject_before_launch():
 
 
 def test_backward_workspace_sizes_and_validation():
-    # expert backward: per-task terms, expert-sorted tasks, per-expert segments
+    # expert backward: per-task terms, expert-sorted tasks, per-expert segments,
+    # and the row order (a key, a sorted position and a 16-byte record per
+    # possible used expert, U_cap = min(N, L*K), plus the sort's key offsets)
     ws = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L=4096, d=2048, K=128,
                                    N=1700416)
     M = 4096 * 128
-    assert ws >= (4 * M + 1700416) * 4 and ws < (12 * M + 1700416 + 4096) * 4
+    assert ws >= (4 * M + 1700416 + 6 * M) * 4 and ws < (18 * M + 1700416 + 4096 + 4096) * 4
     # router backward (bf16): hi/lo logit gradients, their transposes, x^T, W_rc^T
     ws = omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER_BACKWARD, L=4096, d=2048, Nr=1304,
                                    Nc=1304, K=128)

@@ -59,6 +59,11 @@ CASES = [
     (50, 2048, 16, 16, 100, "f32"),  # largest fp32 d
     (40, 64, 8, 8, 64, "bf16"),      # K = N: every expert used by every token
     (70, 128, 20, 20, 1, "bf16"),    # K = 1: gate 1, no router gradient
+    # fewer tokens than XCD classes (the row pass deals the used experts out
+    # by t % 8 of their first token: empty classes, then uneven ones)
+    (1, 128, 8, 8, 32, "f32"),
+    (3, 64, 8, 8, 16, "bf16"),
+    (9, 256, 12, 12, 48, "bf16"),
 ]
 
 
