@@ -153,6 +153,10 @@ def test_backward_workspace_sizes_and_validation():
         with pytest.raises(omni.OmniError) as e:
             omni.omni_workspace_bytes(op, L=4, d=12, Nr=4, Nc=4, K=2, N=16)
         assert e.value.status == omni.OMNI_ERR_UNSUPPORTED
+    # the row pass keys tokens by 8 * ceil(L / 8) + 1 values, which must fit an int32
+    with pytest.raises(omni.OmniError) as e:
+        omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L=2**31 - 8, d=8, K=1, N=16)
+    assert e.value.status == omni.OMNI_ERR_UNSUPPORTED and b"2^31-9" in omni.library().omni_last_error()
     lib = omni.library()
     fake = ctypes.c_void_p(4096)
     s = lib.omni_expert_backward(fake, fake, fake, fake, fake, fake, 4, 8, 16, 2, omni.OMNI_BF16,
