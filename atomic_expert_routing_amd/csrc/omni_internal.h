@@ -90,6 +90,15 @@ __device__ __forceinline__ unsigned wave_umax(unsigned v) { OMNI_ROW_REDUCE(unsi
 __device__ __forceinline__ unsigned wave_umin(unsigned v) { OMNI_ROW_REDUCE(unsigned, u2i, i2u, min_u) }
 #undef OMNI_ROW_REDUCE
 
+// Orders one wave's LDS accesses where the wave works alone on its data
+// (several waves with separate LDS slices share a workgroup), so no
+// workgroup barrier is needed.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Inclusive prefix sum over the 64 lanes: row_shr steps inside each row of
 // 16 (lanes below the shift add 0), then row broadcasts of lane 15 into
 // rows 1 and 3 and of lane 31 into rows 2 and 3.

@@ -200,14 +200,6 @@ inline int pair_count(int K, int Kr, int Kc) {
 // steps.  Element i of a row / column vector lives in register v = i / 64
 // of lane i % 64.
 
-// Orders this wave's LDS accesses: the wave works alone on its token, so a
-// workgroup barrier is not needed (and several tokens share a workgroup).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Digit search of one radix pass: hist[0..256) counts the keys that match
 // the current prefix by their digit.  Returns the largest digit d whose
 // suffix count sum_{d' >= d} hist[d'] reaches `need`, with that bucket's

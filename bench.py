@@ -22,7 +22,7 @@ kernels, on preallocated buffers) and W + K replays are timed the same way
 replays are about 1.5% slower than eager launches, which already keep the
 GPU busy, so the eager rate is the value by default.
 The roofline entry covers the expert-assembly call (its two kernels:
-expert_act and expert_out), whose algorithmic bytes are the unique W and V
+expert_act and expert_out_w), whose algorithmic bytes are the unique W and V
 rows gathered, x read once, y written once and 12 bytes of task metadata
 per task; the unique expert count is taken from the step's own ids.
 After the timed steps, --cold-steps more steps each follow a 512 MiB device
@@ -549,7 +549,7 @@ def main():
                              "step_events": round(step_ev_ms, 4)},
         "unique_experts": U,
         "roofline": {
-            "kernel": "omni_expert_forward (expert_act + expert_out)",
+            "kernel": "omni_expert_forward (expert_act + expert_out_w)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
