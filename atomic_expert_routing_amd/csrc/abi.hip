@@ -33,6 +33,10 @@ constexpr int64_t I32_LIMIT = 2147483647;
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Group size as the kernels take it: every B >= N puts all N experts in
+// group 0, exactly as B = N does, so B is clamped to N (which fits an int).
+int group_size(int64_t B, int64_t N) { return (int)(B < N ? B : N); }
+
 omni_status check_dtype_d(omni_dtype dt, int64_t d) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return fail(OMNI_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (d <= 0) return fail(OMNI_ERR_INVALID_ARG, "d must be positive (got %lld)", (long long)d);
@@ -73,7 +77,10 @@ omni_status schedule_ws(int64_t L, int64_t K, int64_t N, int64_t B, size_t* out)
   if (N <= 0 || B <= 0)
     return fail(OMNI_ERR_INVALID_ARG, "N and B must be positive (N=%lld B=%lld)", (long long)N, (long long)B);
   if (N > I32_LIMIT) return fail(OMNI_ERR_UNSUPPORTED, "N = %lld exceeds 2^31-1", (long long)N);
-  *out = omni::plan_schedule(L, K, N, B).ws_bytes;
+  if (B > I32_LIMIT)
+    return fail(OMNI_ERR_UNSUPPORTED, "B = %lld exceeds 2^31-1 (any B >= N gives one group)",
+                (long long)B);
+  *out = omni::plan_schedule(L, K, N, group_size(B, N)).ws_bytes;
   return OMNI_OK;
 }
 
@@ -210,13 +217,14 @@ omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K, int64_t N, i
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  const int Bi = group_size(B, N);
   if (perm) {
-    const omni::SchedPlan plan = omni::plan_schedule(L, K, N, B);
-    e = omni::launch_schedule(idx, plan.M, (int)B, plan.G, plan, perm, group_off, ws, st);
+    const omni::SchedPlan plan = omni::plan_schedule(L, K, N, Bi);
+    e = omni::launch_schedule(idx, plan.M, Bi, plan.G, plan, perm, group_off, ws, st);
     if (e != hipSuccess) return hip_status(e, "schedule launch");
   }
   if (!token_order) return ok();
-  e = omni::launch_token_order(idx, (int)L, (int)K, N, (int)B, token_order, ws, st);
+  e = omni::launch_token_order(idx, (int)L, (int)K, N, Bi, token_order, ws, st);
   return hip_status(e, "token order launch");
 }
 

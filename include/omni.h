@@ -138,9 +138,10 @@ OMNI_API omni_status omni_router(const void* x, const void* Wr, const void* Wc,
  *                                  output pass that puts tokens sharing their
  *                                  leading experts side by side; it never
  *                                  changes y.
- * Bit-exact and deterministic.  Requires N >= 1, B >= 1, L*K < 2^31,
- * N < 2^31 (and L <= 2^31-8 with token_order).  Workspace: sort buffers,
- * O(L*K) int32.
+ * Bit-exact and deterministic.  Requires N >= 1, 1 <= B < 2^31 (every
+ * B >= N gives the single group 0), L*K < 2^31, N < 2^31 (and
+ * L <= 2^31-8 with token_order); B >= 2^31 is OMNI_ERR_UNSUPPORTED.
+ * Workspace: sort buffers, O(L*K) int32.
  */
 OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
                           int64_t N, int64_t B,

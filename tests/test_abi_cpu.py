@@ -102,6 +102,26 @@ def test_schedule_validation():
         omni.omni_workspace_bytes(9)
 
 
+@pytest.mark.parametrize("B", [2**31, 2**32, 2**32 + 5, 2**62])
+def test_schedule_rejects_group_sizes_beyond_int32(B):
+    """B is taken as an int by the kernels: B >= 2^31 is refused on the host
+    (such a B would otherwise wrap to 0, INT_MIN or a small divisor)."""
+    with pytest.raises(omni.OmniError) as e:
+        omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=4, K=2, N=100, B=B)
+    assert e.value.status == omni.OMNI_ERR_UNSUPPORTED and b"B =" in omni.library().omni_last_error()
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the call fails before any launch
+    s = lib.omni_schedule(fake, 4, 2, 100, B, fake, fake, fake, fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_UNSUPPORTED and b"B =" in lib.omni_last_error()
+
+
+def test_schedule_group_size_at_or_above_n_is_one_group():
+    """Every B >= N (up to 2^31-1) gives G = 1; the workspace equals B = N's."""
+    one = omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=4096, K=128, N=1000, B=1000)
+    for B in (1001, 2**20, 2**31 - 1):
+        assert omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=4096, K=128, N=1000, B=B) == one
+
+
 def test_calls_reject_before_launch():
     """Invalid calls return an error and a message without touching the GPU."""
     lib = omni.library()
