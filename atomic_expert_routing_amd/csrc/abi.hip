@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "omni_internal.h"
 
@@ -179,6 +180,81 @@ omni_status check_ws(const void* ws, size_t have, size_t need) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// omni_schedule's checks apart from the workspace; *need = its workspace size
+omni_status schedule_args(const int32_t* idx, int64_t L, int64_t K, int64_t N, int64_t B,
+                          const int32_t* perm, const int32_t* group_off,
+                          const int32_t* token_order, size_t* need) {
+  omni_status s = schedule_ws(L, K, N, B, need);
+  if (s != OMNI_OK) return s;
+  if (!idx) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL idx");
+  if (!perm != !group_off)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: perm and group_off go together");
+  if (!perm && !token_order) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: no output");
+  if (token_order && L > I32_LIMIT - 7)
+    return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
+  return OMNI_OK;
+}
+
+// The schedule's launches on validated arguments; ws holds the sort buffers.
+omni_status schedule_launch(const int32_t* idx, int64_t L, int64_t K, int64_t N, int64_t B,
+                            int32_t* perm, int32_t* group_off, int32_t* token_order, void* ws,
+                            hipStream_t st) {
+  hipError_t e = hipSuccess;
+  const int Bi = group_size(B, N);
+  if (perm) {
+    const omni::SchedPlan plan = omni::plan_schedule(L, K, N, Bi);
+    e = omni::launch_schedule(idx, plan.M, Bi, plan.G, plan, perm, group_off, ws, st);
+    if (e != hipSuccess) return hip_status(e, "schedule launch");
+  }
+  if (!token_order) return ok();
+  e = omni::launch_token_order(idx, (int)L, (int)K, N, Bi, token_order, ws, st);
+  return hip_status(e, "token order launch");
+}
+
+// ----------------------------------------------------------------- allocation-free schedule
+// omni_schedule_noalloc keeps the sort buffers in this fixed device array
+// instead of a caller workspace.  The code object gives every GPU it is
+// loaded on its own copy, held until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in: the device address of a GPU's
+// copy comes from hipGetSymbolAddress (looked up once per device, with that
+// device current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[OMNI_SCHEDULE_NOALLOC_MAX_WS];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the device that runs `st`.
+omni_status scratch_address(hipStream_t st, void** out) {
+  int dev = -1, cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "omni_schedule_noalloc: hipGetDevice");
+  dev = cur;
+  if (st) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return hip_status(e, "omni_schedule_noalloc: hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(OMNI_ERR_UNSUPPORTED, "omni_schedule_noalloc: device %d beyond %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return hip_status(e, "omni_schedule_noalloc: hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return hip_status(e, "omni_schedule_noalloc: hipGetSymbolAddress");
+    if (!p || (uintptr_t)p % 256)
+      return fail(OMNI_ERR_HIP, "omni_schedule_noalloc: scratch address %p unusable", p);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return OMNI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,26 +282,27 @@ omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K, int64_t N, i
                           int32_t* perm, int32_t* group_off, int32_t* token_order, void* ws,
                           size_t ws_bytes, void* stream) {
   size_t need = 0;
-  omni_status s = schedule_ws(L, K, N, B, &need);
+  omni_status s = schedule_args(idx, L, K, N, B, perm, group_off, token_order, &need);
   if (s != OMNI_OK) return s;
-  if (!idx) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: NULL idx");
-  if (!perm != !group_off)
-    return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: perm and group_off go together");
-  if (!perm && !token_order) return fail(OMNI_ERR_INVALID_ARG, "omni_schedule: no output");
-  if (token_order && L > I32_LIMIT - 7)
-    return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  return schedule_launch(idx, L, K, N, B, perm, group_off, token_order, ws, (hipStream_t)stream);
+}
+
+omni_status omni_schedule_noalloc(const int32_t* idx, int64_t L, int64_t K, int64_t N, int64_t B,
+                                  int32_t* perm, int32_t* group_off, int32_t* token_order,
+                                  void* stream) {
+  size_t need = 0;
+  omni_status s = schedule_args(idx, L, K, N, B, perm, group_off, token_order, &need);
+  if (s != OMNI_OK) return s;
+  if (need > (size_t)OMNI_SCHEDULE_NOALLOC_MAX_WS)
+    return fail(OMNI_ERR_UNSUPPORTED,
+                "omni_schedule_noalloc: these sizes need %zu bytes of scratch, above the fixed "
+                "%zu (use omni_schedule with a workspace)",
+                need, (size_t)OMNI_SCHEDULE_NOALLOC_MAX_WS);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  const int Bi = group_size(B, N);
-  if (perm) {
-    const omni::SchedPlan plan = omni::plan_schedule(L, K, N, Bi);
-    e = omni::launch_schedule(idx, plan.M, Bi, plan.G, plan, perm, group_off, ws, st);
-    if (e != hipSuccess) return hip_status(e, "schedule launch");
-  }
-  if (!token_order) return ok();
-  e = omni::launch_token_order(idx, (int)L, (int)K, N, Bi, token_order, ws, st);
-  return hip_status(e, "token order launch");
+  void* ws = nullptr;
+  if ((s = scratch_address(st, &ws)) != OMNI_OK) return s;
+  return schedule_launch(idx, L, K, N, B, perm, group_off, token_order, ws, st);
 }
 
 omni_status omni_expert_forward(const void* x, const void* W, const void* V, const int32_t* idx,

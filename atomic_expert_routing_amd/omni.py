@@ -16,14 +16,14 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 7
+_ABI_VERSION = 8
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
 OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED, OMNI_OP_EXPERT_BACKWARD_BLOCKED = 6, 7, 8
-EXPORTED = ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
+EXPORTED = ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_blocked",
             "omni_expert_backward_blocked",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
             "omni_shared_mlp", "omni_dense_router", "omni_workspace_bytes", "omni_status_string",
@@ -53,6 +53,7 @@ def library() -> ctypes.CDLL:
     lib.omni_router.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
                                 vp, vp, vp, vp, sz, vp]
     lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.omni_schedule_noalloc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -73,7 +74,7 @@ def library() -> ctypes.CDLL:
                                       sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
-    for f in ("omni_router", "omni_schedule", "omni_expert_forward", "omni_expert_forward_blocked",
+    for f in ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_blocked",
               "omni_expert_backward_blocked",
               "omni_expert_forward_token_centric", "omni_expert_backward",
               "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
@@ -192,6 +193,30 @@ def omni_schedule(idx, N: int, B: int, perm=None, group_off=None, ws=None, strea
     pw, nw = _workspace(ws, need, idx.device)
     _check(library().omni_schedule(pi, L, K, N, B, pp, po, pt, pw, nw, _stream(stream)),
            "omni_schedule")
+    return (perm, group_off) if token_order is None else (perm, group_off, token_order)
+
+
+def omni_schedule_noalloc(idx, N: int, B: int, perm=None, group_off=None, stream=None,
+                          token_order=None, tasks=True):
+    """omni_schedule with its sort buffers in the library's fixed per-GPU
+    scratch array (no workspace argument; the C call allocates nothing).
+    Same arguments and returns as omni_schedule without ws."""
+    L, K = idx.shape
+    G = -(-N // B)
+    pi = _dev(idx, "idx", torch.int32)
+    kw = dict(device=idx.device, dtype=torch.int32)
+    if tasks:
+        perm = torch.empty((L * K,), **kw) if perm is None else perm
+        group_off = torch.empty((G + 1,), **kw) if group_off is None else group_off
+        pp = _dev(perm, "perm", torch.int32, (L * K,))
+        po = _dev(group_off, "group_off", torch.int32, (G + 1,))
+    else:
+        perm = group_off = pp = po = None
+    if token_order is True:
+        token_order = torch.empty((L,), **kw)
+    pt = None if token_order is None else _dev(token_order, "token_order", torch.int32, (L,))
+    _check(library().omni_schedule_noalloc(pi, L, K, N, B, pp, po, pt, _stream(stream)),
+           "omni_schedule_noalloc")
     return (perm, group_off) if token_order is None else (perm, group_off, token_order)
 
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 7
+#define OMNI_ABI_VERSION 8
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -147,6 +147,33 @@ OMNI_API omni_status omni_schedule(const int32_t* idx, int64_t L, int64_t K,
                           int64_t N, int64_t B,
                           int32_t* perm, int32_t* group_off, int32_t* token_order,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omni_schedule_noalloc - omni_schedule for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, outputs, checks and results as omni_schedule (bit for
+ * bit), without ws / ws_bytes: the sort buffers live in a fixed array of
+ * OMNI_SCHEDULE_NOALLOC_MAX_WS bytes inside the library's code object, one
+ * copy per GPU, held until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Sizes whose workspace
+ * (omni_workspace_bytes(OMNI_OP_SCHEDULE, ...)) exceeds that maximum are
+ * refused with OMNI_ERR_UNSUPPORTED before anything is launched: the
+ * 80 MiB cover up to about 4.9 million tasks (L*K), e.g. 16384 tokens x
+ * K = 256.
+ * Every call on one GPU uses that GPU's single array, which keeps whatever
+ * the last call left there (every word the kernels read is written earlier
+ * in the same call, so nothing needs clearing): two calls that may overlap
+ * on one GPU (different streams without an ordering event, or different
+ * host threads) race on it and give undefined results.  The first call on a
+ * device looks the array's device address up once (hipGetSymbolAddress).
+ */
+#define OMNI_SCHEDULE_NOALLOC_MAX_WS (80u << 20) /* bytes of scratch per GPU */
+OMNI_API omni_status omni_schedule_noalloc(const int32_t* idx, int64_t L, int64_t K,
+                                           int64_t N, int64_t B, int32_t* perm,
+                                           int32_t* group_off, int32_t* token_order,
+                                           void* stream);
 
 /*
  * omni_expert_forward - Dynamic Expert Assembly over the schedule.

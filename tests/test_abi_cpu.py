@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 7
+    assert lib.omni_abi_version() == 8
 
 
 def test_status_strings():
@@ -289,3 +289,24 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         omni.omni_router(x, torch.zeros(2, 8), torch.zeros(2, 8), 2)
+
+
+def test_noalloc_schedule_rejects_before_touching_the_gpu():
+    """omni_schedule_noalloc runs omni_schedule's checks, then refuses sizes
+    whose sort buffers exceed its fixed scratch; all before any HIP call."""
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    s = lib.omni_schedule_noalloc(None, 4, 2, 100, 8, fake, fake, None, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL idx" in lib.omni_last_error()
+    s = lib.omni_schedule_noalloc(fake, 4, 2, 100, 2**32 + 5, fake, fake, None, None)
+    assert s == omni.OMNI_ERR_UNSUPPORTED and b"B =" in lib.omni_last_error()
+    s = lib.omni_schedule_noalloc(fake, 4, 2, 100, 8, fake, None, None, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"together" in lib.omni_last_error()
+    # 16384 x 512 tasks need about 129 MiB of sort buffers: above the 80 MiB
+    need = omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=16384, K=512, N=1700416, B=256)
+    assert need > 80 << 20
+    s = lib.omni_schedule_noalloc(fake, 16384, 512, 1700416, 256, fake, fake, None, None)
+    assert s == omni.OMNI_ERR_UNSUPPORTED and b"scratch" in lib.omni_last_error()
+    # the largest configured workload (16384 x 256 tasks) fits
+    assert omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=16384, K=256, N=1700416,
+                                     B=256) <= 80 << 20
