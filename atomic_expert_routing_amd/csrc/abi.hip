@@ -96,6 +96,21 @@ omni_status expert_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt,
   return OMNI_OK;
 }
 
+// omni_expert_forward: the activations [L*K] fp32, then the activation
+// pass's chunk starts [ceil(L*K / chunk) + 1] int32
+omni_status expert_fwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B, omni_dtype dt,
+                          size_t* out) {
+  omni_status s;
+  if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
+  if (B <= 0) return fail(OMNI_ERR_INVALID_ARG, "B must be positive (got %lld)", (long long)B);
+  if (B > I32_LIMIT)
+    return fail(OMNI_ERR_UNSUPPORTED, "B = %lld exceeds 2^31-1 (any B >= N gives one group)",
+                (long long)B);
+  *out = align256((size_t)L * (size_t)K * 4) +
+         align256(((size_t)omni::expert_act_chunks(L * K) + 1) * 4);
+  return OMNI_OK;
+}
+
 omni_status expert_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
   omni_status s;
   if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
@@ -306,14 +321,14 @@ omni_status omni_schedule_noalloc(const int32_t* idx, int64_t L, int64_t K, int6
 }
 
 omni_status omni_expert_forward(const void* x, const void* W, const void* V, const int32_t* idx,
-                                const float* gate, const int32_t* perm,
+                                const float* gate, const int32_t* perm, const int32_t* group_off,
                                 const int32_t* token_order, int64_t L, int64_t d, int64_t N,
-                                int64_t K, omni_dtype dt, float* y, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                int64_t K, int64_t B, omni_dtype dt, float* y, void* ws,
+                                size_t ws_bytes, void* stream) {
   size_t need = 0;
-  omni_status s = expert_ws(L, d, N, K, dt, &need);
+  omni_status s = expert_fwd_ws(L, d, N, K, B, dt, &need);
   if (s != OMNI_OK) return s;
-  if (!x || !W || !V || !idx || !gate || !perm || !y)
+  if (!x || !W || !V || !idx || !gate || !perm || !group_off || !y)
     return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: NULL array pointer");
   if (token_order && L > I32_LIMIT - 7)
     return fail(OMNI_ERR_UNSUPPORTED, "token order needs L <= 2^31-8 (L=%lld)", (long long)L);
@@ -321,8 +336,12 @@ omni_status omni_expert_forward(const void* x, const void* W, const void* V, con
     return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward: x, W, V and y must be 16-byte aligned");
   if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  const int Bi = group_size(B, N);
+  const int G = (int)((N + Bi - 1) / Bi);
   float* act = (float*)ws;
-  hipError_t e = omni::launch_expert_act(x, W, idx, gate, perm, (int)L, (int)d, (int)K, dt, act, st);
+  int32_t* start = (int32_t*)((char*)ws + align256((size_t)L * (size_t)K * 4));
+  hipError_t e = omni::launch_expert_act(x, W, idx, gate, perm, group_off, (int)L, (int)d, (int)K,
+                                         Bi, G, dt, act, start, st);
   if (e != hipSuccess) return hip_status(e, "expert activation launch");
   e = omni::launch_expert_out(V, idx, act, token_order, (int)L, (int)d, (int)K, dt, y, st);
   return hip_status(e, "expert output launch");
@@ -480,7 +499,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
   switch (op) {
     case OMNI_OP_ROUTER: s = router_ws(L, d, Nr, Nc, K, dt, &need); break;
     case OMNI_OP_SCHEDULE: s = schedule_ws(L, K, N, B, &need); break;
-    case OMNI_OP_EXPERT_FORWARD: s = expert_ws(L, d, N, K, dt, &need); break;
+    case OMNI_OP_EXPERT_FORWARD: s = expert_fwd_ws(L, d, N, K, B, dt, &need); break;
     case OMNI_OP_EXPERT_BACKWARD: s = expert_bwd_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_ROUTER_BACKWARD: s = router_bwd_ws(L, d, Nr, Nc, K, dt, &need); break;
     case OMNI_OP_SHARED_MLP: s = mlp_ws(L, d, N, dt, &need); break;

@@ -73,50 +73,81 @@ __device__ __forceinline__ float uni(float v) {
 }
 
 // ------------------------------------------------------------------ expert_act
+// The activation pass walks the schedule group by group.  act_plan cuts the
+// sorted tasks into chunks along group boundaries: chunk c starts at the
+// first group boundary in [c*ACT_CHUNK, (c+1)*ACT_CHUNK) (found from the
+// group of that position, idx/B, and group_off), or at c*ACT_CHUNK when one
+// group covers that whole window (a group larger than a chunk is split).
+// A chunk so holds whole groups (1 to 2*ACT_CHUNK-1 tasks), and all tasks of
+// one group and token class run in one wave, next to each other in time:
+// a W row that several of them use is fetched once and served from the
+// cache to the others.
+//
 // The 8 XCDs of an MI355X each have their own L2 and workgroup i runs on XCD
-// i % 8.  The scheduled task stream is cut into chunks of ACT_CHUNK tasks;
-// chunk c is visited by the 8 one-wave workgroups 8c .. 8c+7, and workgroup
-// 8c+x takes the chunk's tasks whose token t has t % 8 == x.  Each XCD so
-// reads the x rows of one eighth of the tokens, a set that stays resident
-// in its L2, while the stream order inside the chunk (group, then token)
-// is kept.  The wave's tasks are compacted into LDS; the W row of the next
-// task is in flight while the current one is reduced (two row buffers).
-// Measured on the 4096-token, 1.7M-expert workload: chunks of 8 to 32 tasks
-// are equally fast and 128 is 10% slower; without the XCD split the x rows
-// fall out of L2 and the pass is 15% slower; plain loads of W beat
-// non-temporal ones (repeated experts of a group can hit in the caches).
+// i % 8.  Chunk c is visited by the 8 one-wave workgroups 8c .. 8c+7, and
+// workgroup 8c+x takes the chunk's tasks whose token t has t % 8 == x.  Each
+// XCD so reads the x rows of one eighth of the tokens, a set that stays
+// resident in its L2, while the stream order inside the chunk (group, then
+// token) is kept.  The wave's tasks are compacted into LDS; the W row of
+// the next task is in flight while the current one is reduced (two row
+// buffers).  Measured on the 4096-token, 1.7M-expert workload: chunks of 8
+// to 32 tasks are equally fast and 128 is 10% slower; without the XCD split
+// the x rows fall out of L2 and the pass is 15% slower; plain loads of W
+// beat non-temporal ones (repeated experts of a group hit in the caches).
 constexpr int ACT_CHUNK = 32;
 constexpr int XCDS = 8;
+
+__global__ __launch_bounds__(256) void act_plan(const int32_t* __restrict__ idx,
+                                                const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ group_off, int M,
+                                                int B, int G, int nchunks,
+                                                int32_t* __restrict__ start) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c > nchunks) return;
+  const int p = c * ACT_CHUNK;
+  int s = M;
+  if (p < M) {
+    // ids outside [0, N) break the precondition; clamping keeps the reads in bounds
+    const int g = min(max(idx[perm[p]] / B, 0), G - 1);
+    const int a = group_off[g];
+    if (a == p) {
+      s = p;
+    } else {
+      const int b = group_off[g + 1];
+      s = (b > p && b < p + ACT_CHUNK) ? b : p;
+    }
+  }
+  start[c] = s;
+}
 
 template <bool BF16, int NCH>
 __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_,
                                                  const uint16_t* __restrict__ W_,
                                                  const int32_t* __restrict__ idx,
                                                  const float* __restrict__ gate,
-                                                 const int32_t* __restrict__ perm, int M, int d,
-                                                 int K, float* __restrict__ act) {
+                                                 const int32_t* __restrict__ perm,
+                                                 const int32_t* __restrict__ start, int d, int K,
+                                                 float* __restrict__ act) {
   using V = Vec<BF16>;
-  __shared__ int sm[ACT_CHUNK];
-  __shared__ int se[ACT_CHUNK];
-  __shared__ float sg[ACT_CHUNK];
+  __shared__ int sm[2 * ACT_CHUNK];
+  __shared__ int se[2 * ACT_CHUNK];
+  __shared__ float sg[2 * ACT_CHUNK];
+  static_assert(2 * ACT_CHUNK <= 64, "one lane per task of a chunk");
   const int lane = threadIdx.x;
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int chunk = blockIdx.x / XCDS, part = blockIdx.x % XCDS;
-  const int p0 = chunk * ACT_CHUNK;
-  const int n = min(ACT_CHUNK, M - p0);
-  int cnt = 0;
-  for (int h = 0; h < ACT_CHUNK; h += 64) {  // ACT_CHUNK <= 64: one pass
-    const bool v = h + lane < n;
-    const int m = v ? perm[p0 + h + lane] : 0;
-    const bool mine = v && (m / K) % XCDS == part;
-    const unsigned long long b = __ballot(mine);
-    if (mine) {
-      const int pos = cnt + __popcll(b & lt);
-      sm[pos] = m;
-      se[pos] = idx[m];
-      sg[pos] = gate[m];
-    }
-    cnt += __popcll(b);
+  const int p0 = start[chunk];
+  const int n = start[chunk + 1] - p0;  // 0 .. 2*ACT_CHUNK-1
+  const bool v = lane < n;
+  const int m = v ? perm[p0 + lane] : 0;
+  const bool mine = v && (m / K) % XCDS == part;
+  const unsigned long long b = __ballot(mine);
+  const int cnt = __popcll(b);
+  if (mine) {
+    const int pos = __popcll(b & lt);
+    sm[pos] = m;
+    se[pos] = idx[m];
+    sg[pos] = gate[m];
   }
   if (cnt == 0) return;
   __syncthreads();
@@ -143,9 +174,9 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
   u32x4 xr[NCH], wa[NCH], wb[NCH];
   int t_cur = -1;
   auto step = [&](int i, const u32x4* w) {
-    const int m = uni(sm[i]);
+    const int mi = uni(sm[i]);
     const float g = uni(sg[i]);
-    const int t = m / K;
+    const int t = mi / K;
     if (t != t_cur) {  // consecutive tasks of one token reuse its x row
       load_x(t, xr);
       t_cur = t;
@@ -154,7 +185,7 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
 #pragma unroll
     for (int c = 0; c < NCH; ++c) part_sum += V::dot(xr[c], w[c]);
     const float h = wave_sum(part_sum);
-    if (lane == 0) act[m] = g * (h / (1.f + expf(-h)));
+    if (lane == 0) act[mi] = g * (h / (1.f + expf(-h)));
   };
   load_w(uni(se[0]), wa);
   for (int i = 0; i < cnt; i += 2) {
@@ -414,16 +445,20 @@ hipError_t launch_tc_t(const void* x, const void* W, const void* V, const int32_
 
 template <bool BF16>
 hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const float* gate,
-                        const int32_t* perm, int M, int d, int K, float* act, hipStream_t s) {
+                        const int32_t* perm, const int32_t* group_off, int M, int d, int K, int B,
+                        int G, float* act, int32_t* start, hipStream_t s) {
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
   const int nch = (int)((row_bytes + 1023) / 1024);
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* wp = (const uint16_t*)W;
-  const dim3 grid((unsigned)(((M + ACT_CHUNK - 1) / ACT_CHUNK) * XCDS)), block(64);
+  const int nchunks = (M + ACT_CHUNK - 1) / ACT_CHUNK;
+  hipLaunchKernelGGL(act_plan, dim3((nchunks + 1 + 255) / 256), dim3(256), 0, s, idx, perm,
+                     group_off, M, B, G, nchunks, start);
+  const dim3 grid((unsigned)(nchunks * XCDS)), block(64);
 #define OMNI_ACT(N)                                                                          \
   case N:                                                                                    \
-    hipLaunchKernelGGL((expert_act<BF16, N>), grid, block, 0, s, xp, wp, idx, gate, perm, M, \
-                       d, K, act);                                                           \
+    hipLaunchKernelGGL((expert_act<BF16, N>), grid, block, 0, s, xp, wp, idx, gate, perm,    \
+                       start, d, K, act);                                                    \
     break;
   switch (nch) {
     OMNI_ACT(1) OMNI_ACT(2) OMNI_ACT(3) OMNI_ACT(4) OMNI_ACT(5) OMNI_ACT(6) OMNI_ACT(7)
@@ -437,12 +472,16 @@ hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const 
 
 }  // namespace
 
+int expert_act_chunks(int64_t M) { return (int)((M + ACT_CHUNK - 1) / ACT_CHUNK); }
+
 hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, const float* gate,
-                             const int32_t* perm, int L, int d, int K, omni_dtype dt, float* act,
+                             const int32_t* perm, const int32_t* group_off, int L, int d, int K,
+                             int B, int G, omni_dtype dt, float* act, int32_t* start,
                              hipStream_t s) {
   const int M = L * K;
-  return dt == OMNI_BF16 ? launch_act_t<true>(x, W, idx, gate, perm, M, d, K, act, s)
-                         : launch_act_t<false>(x, W, idx, gate, perm, M, d, K, act, s);
+  return dt == OMNI_BF16
+             ? launch_act_t<true>(x, W, idx, gate, perm, group_off, M, d, K, B, G, act, start, s)
+             : launch_act_t<false>(x, W, idx, gate, perm, group_off, M, d, K, B, G, act, start, s);
 }
 
 hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,

@@ -179,10 +179,14 @@ hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
                               int32_t* order, void* ws, hipStream_t s);
 
-// act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order
+// act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order, in
+// chunks along the group boundaries of group_off (B experts per group, G
+// groups); start [expert_act_chunks(L*K) + 1] int32 is workspace
+int expert_act_chunks(int64_t M);
 hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, const float* gate,
-                             const int32_t* perm, int L, int d, int K, omni_dtype dt,
-                             float* act, hipStream_t s);
+                             const int32_t* perm, const int32_t* group_off, int L, int d, int K,
+                             int B, int G, omni_dtype dt, float* act, int32_t* start,
+                             hipStream_t s);
 // token-centric baseline: y[t] = sum_k gate * SiLU(x_t . W[e]) * V[e], one token per workgroup
 hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,
                             const float* gate, int L, int d, int K, omni_dtype dt, float* y,

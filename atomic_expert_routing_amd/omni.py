@@ -16,7 +16,7 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 8
+_ABI_VERSION = 9
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
@@ -54,8 +54,8 @@ def library() -> ctypes.CDLL:
                                 vp, vp, vp, vp, sz, vp]
     lib.omni_schedule.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.omni_schedule_noalloc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp]
-    lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
-                                        ctypes.c_int, vp, vp, sz, vp]
+    lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                        i64, ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                 ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -220,15 +220,17 @@ def omni_schedule_noalloc(idx, N: int, B: int, perm=None, group_off=None, stream
     return (perm, group_off) if token_order is None else (perm, group_off, token_order)
 
 
-def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None,
-                        token_order=None):
-    """Dynamic Expert Assembly over the schedule -> y [L, d] float32.
+def omni_expert_forward(x, W, V, idx, gate, perm, group_off, B: int, y=None, ws=None,
+                        stream=None, token_order=None):
+    """Dynamic Expert Assembly over the schedule (perm, group_off of group
+    size B, from omni_schedule) -> y [L, d] float32.
 
     token_order (optional [L] int32, from omni_schedule) sets the order in
     which the output pass visits tokens; y does not depend on it."""
     L, d = x.shape
     N = W.shape[0]
     K = idx.shape[1]
+    G = -(-N // B)
     dt = _dtype_code(x)
     px = _dev(x, "x")
     pW = _dev(W, "W", x.dtype, (N, d))
@@ -236,13 +238,14 @@ def omni_expert_forward(x, W, V, idx, gate, perm, y=None, ws=None, stream=None,
     pi = _dev(idx, "idx", torch.int32, (L, K))
     pg = _dev(gate, "gate", torch.float32, (L, K))
     pp = _dev(perm, "perm", torch.int32, (L * K,))
+    po = _dev(group_off, "group_off", torch.int32, (G + 1,))
     pt = None if token_order is None else _dev(token_order, "token_order", torch.int32, (L,))
     y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
     py = _dev(y, "y", torch.float32, (L, d))
-    need = omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
+    need = omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, L, d, 1, 1, K, N, B, dt) if ws is None else 0
     pw, nw = _workspace(ws, need, x.device)
-    _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, pt, L, d, N, K, dt, py, pw, nw,
-                                         _stream(stream)), "omni_expert_forward")
+    _check(library().omni_expert_forward(px, pW, pV, pi, pg, pp, po, pt, L, d, N, K, B, dt, py,
+                                         pw, nw, _stream(stream)), "omni_expert_forward")
     return y
 
 
@@ -455,8 +458,8 @@ class RoutedBranch:
         if self.assembly == "blocked":
             return omni_expert_forward_blocked(x, W, V, self.idx, self.gate, self.token_order,
                                                self.y, self.ws, stream)
-        return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.y, self.ws, stream,
-                                   self.token_order)
+        return omni_expert_forward(x, W, V, self.idx, self.gate, self.perm, self.group_off, self.B,
+                                   self.y, self.ws, stream, self.token_order)
 
     def forward(self, x, Wr, Wc, W, V, stream=None):
         self.router(x, Wr, Wc, stream)

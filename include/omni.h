@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 8
+#define OMNI_ABI_VERSION 9
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -186,7 +186,9 @@ OMNI_API omni_status omni_schedule_noalloc(const int32_t* idx, int64_t L, int64_
  *   W, V  [N, d]  dtype dt    row e holds atomic expert e's input / output vector
  *   idx   [L, K]  int32       expert ids (from omni_router)
  *   gate  [L, K]  fp32        gates      (from omni_router)
- *   perm  [L*K]   int32       schedule   (from omni_schedule)
+ *   perm  [L*K]   int32       schedule   (from omni_schedule, same B)
+ *   group_off [G+1] int32     group offsets (from omni_schedule, same B),
+ *                             G = ceil(N/B)
  *   token_order [L] int32     optional (NULL: tokens by id); the order in which
  *                             the output pass visits tokens, each of the 8
  *                             XCDs taking a contiguous eighth (from
@@ -194,20 +196,31 @@ OMNI_API omni_status omni_schedule_noalloc(const int32_t* idx, int64_t L, int64_
  *                             permutation of [0, L): entries outside [0, L)
  *                             are skipped and a token that never appears keeps
  *                             its old y row.  y itself does not depend on it.
+ *   B                         group size the schedule was built with
+ *                             (1 <= B < 2^31; every B >= N is one group)
  *   y     [L, d]  fp32 out    y_t = sum_k gate[t,k] * SiLU(x_t . W[idx[t,k]]) * V[idx[t,k]]
  *                             fully overwritten (no accumulation into old y)
- * SiLU(h) = h / (1 + exp(-h)).  The activation pass walks the tasks in
- * schedule order (expert-centric: a group's weight rows are read once and
- * reused by its tokens); the output pass sums each token's K terms in k
- * order without atomics, so y is deterministic.
+ * SiLU(h) = h / (1 + exp(-h)).  The activation pass walks the scheduled tasks
+ * group by group: the sorted tasks are cut into chunks along the group
+ * boundaries that group_off gives (a group larger than a chunk is split), so
+ * a group's tasks of one token class run in one wave, one after another, and
+ * a W row that several of them use is fetched once; each task's gated
+ * activation g * SiLU(x_t . W[e]) is the (G_q . sigma(X_q W_q^T)) factor.
+ * The output pass then sums each token's K terms a V[e] in k order without
+ * atomics, so y is deterministic.  perm and group_off must be the schedule of
+ * this idx with this B (they are read, not checked: other values give other
+ * sums, never an out-of-bounds access as long as perm is a permutation of
+ * [0, L*K) and group_off is non-decreasing from 0 to L*K).
  * Requires d % 8 == 0, d <= OMNI_MAX_D_BF16 (bf16) or OMNI_MAX_D_F32 (fp32),
- * K <= OMNI_MAX_K, L*K < 2^31, N < 2^31.  Workspace: fp32 activations [L*K].
+ * K <= OMNI_MAX_K, L*K < 2^31, N < 2^31.  Workspace: fp32 activations [L*K]
+ * and the chunk starts (omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD, ...,
+ * B, ...)).
  */
 OMNI_API omni_status omni_expert_forward(const void* x, const void* W, const void* V,
                                 const int32_t* idx, const float* gate,
-                                const int32_t* perm, const int32_t* token_order,
-                                int64_t L, int64_t d, int64_t N, int64_t K,
-                                omni_dtype dt, float* y,
+                                const int32_t* perm, const int32_t* group_off,
+                                const int32_t* token_order, int64_t L, int64_t d, int64_t N,
+                                int64_t K, int64_t B, omni_dtype dt, float* y,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 8
+    assert lib.omni_abi_version() == 9
 
 
 def test_status_strings():
@@ -48,9 +48,14 @@ def test_workspace_sizes():
     # router: fp32 logits [L, N_r + N_c], 256-byte aligned
     assert omni.omni_workspace_bytes(omni.OMNI_OP_ROUTER, L=4096, d=2048, Nr=1304, Nc=1304,
                                      K=128) == 4096 * 2608 * 4
-    # expert forward: fp32 activations [L*K]
+    # expert forward: fp32 activations [L*K], then the activation pass's chunk
+    # starts (one per 32 scheduled tasks, plus the end), each part 256-byte aligned
+    M = 4096 * 128
     assert omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4096, d=2048, K=128,
-                                     N=1700416) == 4096 * 128 * 4
+                                     N=1700416, B=128) == M * 4 + -(-(M // 32 + 1) * 4 // 256) * 256
+    for B in (0, 2**31):
+        with pytest.raises(omni.OmniError):
+            omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=4, d=64, K=2, N=100, B=B)
     # schedule: four O(M) int32 sort buffers plus the digit table
     ws = omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=4096, K=128, N=1700416, B=128)
     assert 4 * 4096 * 128 * 4 <= ws < 5 * 4096 * 128 * 4
@@ -144,8 +149,8 @@ def test_calls_reject_before_launch():
     s = lib.omni_schedule(fake, 4, 2, 10, 2, None, None, None, fake, 1 << 20, None)
     assert s == omni.OMNI_ERR_INVALID_ARG and b"no output" in lib.omni_last_error()
     # misaligned x
-    s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, None, 4, 8,
-                                10, 2, omni.OMNI_BF16, fake, fake, 1 << 20, None)
+    s = lib.omni_expert_forward(ctypes.c_void_p(4098), fake, fake, fake, fake, fake, fake, None,
+                                4, 8, 10, 2, 3, omni.OMNI_BF16, fake, fake, 1 << 20, None)
     assert s == omni.OMNI_ERR_INVALID_ARG
     # K larger than the grid
     s = lib.omni_router(fake, fake, fake, 4, 8, 2, 2, 5, omni.OMNI_F32, fake, fake, fake,

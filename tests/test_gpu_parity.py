@@ -137,8 +137,9 @@ def test_expert_forward_on_oracle_routing():
     idx = torch.as_tensor(out["idx"], dtype=torch.int32, device="cuda")
     gate = torch.as_tensor(out["gate"], dtype=torch.float32, device="cuda")
     perm = torch.as_tensor(out["perm"], dtype=torch.int32, device="cuda")
+    off = torch.as_tensor(out["group_off"], dtype=torch.int32, device="cuda")
     say("expert forward on oracle routing")
-    y = omni.omni_expert_forward(g["x"], g["W"], g["V"], idx, gate, perm)
+    y = omni.omni_expert_forward(g["x"], g["W"], g["V"], idx, gate, perm, off, w.B)
     torch.cuda.synchronize()
     # the gate went through fp32 on its way in: compare with the oracle's y
     # for the same fp32 gate values
@@ -172,7 +173,7 @@ def check_token_order(inp, br, w):
     output pass that follows it reproduces br.y bit for bit: each token's
     sum is taken in k order whatever order the tokens run in."""
     perm, off, order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True)
-    y = omni.omni_expert_forward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, perm,
+    y = omni.omni_expert_forward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, perm, off, w.B,
                                  token_order=order)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(order), O.token_order(to_np(br.idx), w.B))
