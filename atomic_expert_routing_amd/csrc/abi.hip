@@ -111,6 +111,15 @@ omni_status expert_fwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B,
   return OMNI_OK;
 }
 
+omni_status expert_auto_ws(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B, omni_dtype dt,
+                           size_t* out) {
+  omni_status s;
+  if ((s = expert_fwd_ws(L, d, N, K, B, dt, out)) != OMNI_OK) return s;
+  if ((s = schedule_ws(L, K, N, B, out)) != OMNI_OK) return s;
+  *out = omni::plan_expert_auto(L, d, N, K, group_size(B, N), dt).ws_bytes;
+  return OMNI_OK;
+}
+
 omni_status expert_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
   omni_status s;
   if ((s = expert_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
@@ -347,6 +356,26 @@ omni_status omni_expert_forward(const void* x, const void* W, const void* V, con
   return hip_status(e, "expert output launch");
 }
 
+omni_status omni_expert_forward_auto(const void* x, const void* W, const void* V,
+                                     const int32_t* idx, const float* gate, int64_t L, int64_t d,
+                                     int64_t N, int64_t K, int64_t B, omni_dtype dt, float* y,
+                                     int32_t* chosen, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = expert_auto_ws(L, d, N, K, B, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !y)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_forward_auto: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(y))
+    return fail(OMNI_ERR_INVALID_ARG,
+                "omni_expert_forward_auto: x, W, V and y must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const int Bi = group_size(B, N);
+  const omni::AutoPlan plan = omni::plan_expert_auto(L, d, N, K, Bi, dt);
+  hipError_t e = omni::launch_expert_auto(x, W, V, idx, gate, (int)L, (int)d, N, (int)K, Bi, dt,
+                                          y, chosen, plan, ws, (hipStream_t)stream);
+  return hip_status(e, "automatic assembly launch");
+}
+
 omni_status omni_expert_forward_blocked(const void* x, const void* W, const void* V,
                                         const int32_t* idx, const float* gate,
                                         const int32_t* token_order, int64_t L, int64_t d,
@@ -491,6 +520,25 @@ omni_status omni_dense_router(const void* x, const void* Wn, int64_t L, int64_t 
   return hip_status(e, "dense router launch");
 }
 
+omni_status omni_gather_probe(const void* A, int64_t n_rows_A, int64_t row_bytes,
+                              const int32_t* rows, int64_t n, float* sink, size_t sink_floats,
+                              void* stream) {
+  if (!A || !rows || !sink) return fail(OMNI_ERR_INVALID_ARG, "omni_gather_probe: NULL pointer");
+  if (!aligned16(A)) return fail(OMNI_ERR_INVALID_ARG, "omni_gather_probe: A must be 16-byte aligned");
+  if (n <= 0 || n_rows_A <= 0)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_gather_probe: n and n_rows_A must be positive");
+  if (row_bytes < 16 || row_bytes > 65536 || row_bytes % 16)
+    return fail(OMNI_ERR_UNSUPPORTED, "omni_gather_probe: row_bytes %lld not a multiple of 16 "
+                "in [16, 65536]", (long long)row_bytes);
+  const size_t need = (size_t)omni::gather_probe_blocks(n) * 256;
+  if (sink_floats < need)
+    return fail(OMNI_ERR_WORKSPACE, "omni_gather_probe: sink of %zu floats, %zu needed",
+                sink_floats, need);
+  hipError_t e = omni::launch_gather_probe(A, n_rows_A, rows, n, (int)row_bytes, sink,
+                                           (hipStream_t)stream);
+  return hip_status(e, "gather probe launch");
+}
+
 omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, int64_t Nc,
                                  int64_t K, int64_t N, int64_t B, omni_dtype dt, size_t* out) {
   if (!out) return fail(OMNI_ERR_INVALID_ARG, "omni_workspace_bytes: out is NULL");
@@ -506,6 +554,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_DENSE_ROUTER: s = dense_router_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_EXPERT_FORWARD_BLOCKED: s = blocked_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_EXPERT_BACKWARD_BLOCKED: s = blocked_bwd_ws(L, d, N, K, dt, &need); break;
+    case OMNI_OP_EXPERT_FORWARD_AUTO: s = expert_auto_ws(L, d, N, K, B, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

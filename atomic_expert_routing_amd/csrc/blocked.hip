@@ -158,7 +158,9 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
                                                   const int32_t* __restrict__ order, int L, int K,
                                                   int ucap, int32_t* __restrict__ U,
                                                   int32_t* __restrict__ nU, float* __restrict__ G,
-                                                  int32_t* __restrict__ kmap) {
+                                                  int32_t* __restrict__ kmap,
+                                                  const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   extern __shared__ __attribute__((aligned(16))) int keys[];
   __shared__ int wtot[16];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
 // toff[b] = column tiles of the blocks before b (toff[nb] = all tiles, the
 // work list of blk_act); block b has toff[b+1] - toff[b] tiles.
 __global__ __launch_bounds__(1024) void blk_plan(const int32_t* __restrict__ nU, int nb,
-                                                 int32_t* __restrict__ toff) {
+                                                 int32_t* __restrict__ toff,
+                                                 const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int wtot[16];
   const int tid = threadIdx.x;
   int carry = 0;
@@ -398,7 +402,9 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
                                                uint16_t* __restrict__ Ahi,
                                                uint16_t* __restrict__ Alo,
                                                float* __restrict__ dgate, float* __restrict__ dh,
-                                               float* __restrict__ ga) {
+                                               float* __restrict__ ga,
+                                               const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm1[];
   constexpr int PHASES = MODE == BLK_FWD ? 1 : 3;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -568,7 +574,9 @@ __global__ __launch_bounds__(256) void blk_out(const uint16_t* __restrict__ V,
                                                const int32_t* __restrict__ toff,
                                                const uint16_t* __restrict__ Ahi,
                                                const uint16_t* __restrict__ Alo, int L, int d,
-                                               int ucap, void* __restrict__ y_) {
+                                               int ucap, void* __restrict__ y_,
+                                               const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm2[];
   constexpr int STAGE = NB * K2_VT + 2 * K2_AT;
   constexpr int OPS = 4 * NB + 2;  // vector loads per wave and k-tile
@@ -890,7 +898,8 @@ namespace {
 
 // blk_union (with the task-slot map when kmap is not null) and blk_plan
 hipError_t launch_union_plan(const int32_t* idx, const float* gate, const int32_t* order, int L,
-                             int K, const BlockedPlan& p, void* ws, int32_t* kmap, hipStream_t s) {
+                             int K, const BlockedPlan& p, void* ws, int32_t* kmap, hipStream_t s,
+                             RunGate run = {}) {
   char* w = (char*)ws;
   int32_t* U = (int32_t*)(w + p.off_U);
   int32_t* nU = (int32_t*)(w + p.off_nU);
@@ -901,7 +910,7 @@ hipError_t launch_union_plan(const int32_t* idx, const float* gate, const int32_
 #define OMNI_BLK_UNION(E)                                                                     \
   case E:                                                                                     \
     hipLaunchKernelGGL(blk_union<E>, dim3(p.nb), dim3(1024), lds_u, s, idx, gate, order, L, \
-                       K, p.ucap, U, nU, G, kmap);                                            \
+                       K, p.ucap, U, nU, G, kmap, run.flag, run.want);                        \
     break;
     OMNI_BLK_UNION(1) OMNI_BLK_UNION(2) OMNI_BLK_UNION(4) OMNI_BLK_UNION(8) OMNI_BLK_UNION(16)
     OMNI_BLK_UNION(32)
@@ -909,7 +918,7 @@ hipError_t launch_union_plan(const int32_t* idx, const float* gate, const int32_
     default:
       return hipErrorInvalidValue;  // K above the validated limit
   }
-  hipLaunchKernelGGL(blk_plan, dim3(1), dim3(1024), 0, s, nU, p.nb, toff);
+  hipLaunchKernelGGL(blk_plan, dim3(1), dim3(1024), 0, s, nU, p.nb, toff, run.flag, run.want);
   return hipGetLastError();
 }
 
@@ -934,21 +943,23 @@ __global__ __launch_bounds__(256) void split_bf16(const float* __restrict__ a, s
 
 hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, const int32_t* idx,
                                  const float* gate, const int32_t* order, int L, int d, int K,
-                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s) {
+                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s,
+                                 RunGate run) {
   char* w = (char*)ws;
   const int32_t* U = (const int32_t*)(w + p.off_U);
   const int32_t* toff = (const int32_t*)(w + p.off_toff);
   const float* G = (const float*)(w + p.off_G);
   uint16_t* Ahi = (uint16_t*)(w + p.off_Ahi);
   uint16_t* Alo = (uint16_t*)(w + p.off_Alo);
-  hipError_t e = launch_union_plan(idx, gate, order, L, K, p, ws, nullptr, s);
+  hipError_t e = launch_union_plan(idx, gate, order, L, K, p, ws, nullptr, s, run);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(blk_act<BLK_FWD>, dim3(act_grid(p)), dim3(256), K1_S * K1_STAGE, s,
                      (const uint16_t*)x, (const uint16_t*)W, nullptr, nullptr, nullptr, order, U,
-                     toff, G, nullptr, L, d, K, p.nb, p.ucap, Ahi, Alo, nullptr, nullptr, nullptr);
+                     toff, G, nullptr, L, d, K, p.nb, p.ucap, Ahi, Alo, nullptr, nullptr, nullptr,
+                     run.flag, run.want);
   hipLaunchKernelGGL((blk_out<false, 1, false>), dim3(p.nb * (d / K2_COLS)), dim3(256),
                      K2_S * K2_STAGE, s, (const uint16_t*)V, nullptr, order, nullptr, U, toff, Ahi,
-                     Alo, L, d, p.ucap, (void*)y);
+                     Alo, L, d, p.ucap, (void*)y, run.flag, run.want);
   return hipGetLastError();
 }
 
@@ -1024,11 +1035,11 @@ hipError_t launch_expert_backward_blocked(const void* x, const void* W, const vo
                      0, s, dy, n, dyh, dyl);
   hipLaunchKernelGGL(blk_act<BLK_BWD>, dim3(act_grid(bp)), dim3(256), K1_S * K1_STAGE, s,
                      (const uint16_t*)x, (const uint16_t*)W, dyh, dyl, (const uint16_t*)V, order, U,
-                     toff, G, kmap, L, d, K, bp.nb, bp.ucap, dHhi, dHlo, dgate, dh, ga);
+                     toff, G, kmap, L, d, K, bp.nb, bp.ucap, dHhi, dHlo, dgate, dh, ga, nullptr, 0);
   // dx = dH W[U], the forward's second product with W in place of V
   hipLaunchKernelGGL((blk_out<false, 1, false>), dim3(bp.nb * (d / K2_COLS)), dim3(256),
                      K2_S * K2_STAGE, s, (const uint16_t*)W, nullptr, order, nullptr, U, toff, dHhi,
-                     dHlo, L, d, bp.ucap, (void*)dx);
+                     dHlo, L, d, bp.ucap, (void*)dx, nullptr, 0);
   // 2. the used experts, then the expert sets and their dW, dV rows
   if ((e = launch_expert_segments(idx, N, uniq, n_uniq, p.bwd, wr, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(inv_order, dim3((L + 255) / 256), dim3(256), 0, s, order, L, pos);
@@ -1049,14 +1060,14 @@ hipError_t launch_expert_backward_blocked(const void* x, const void* W, const vo
   constexpr size_t lds1 = K2_S * (K2_VT + 2 * K2_AT), lds2 = K2_S * (2 * K2_VT + 2 * K2_AT);
   if (obf) {
     hipLaunchKernelGGL((blk_out<true, 1, true>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
-                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows);
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, nullptr, 0);
     hipLaunchKernelGGL((blk_out<true, 2, true>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord, n_uniq,
-                       T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows);
+                       T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, nullptr, 0);
   } else {
     hipLaunchKernelGGL((blk_out<true, 1, false>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
-                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows);
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, nullptr, 0);
     hipLaunchKernelGGL((blk_out<true, 2, false>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord,
-                       n_uniq, T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows);
+                       n_uniq, T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, nullptr, 0);
   }
   return hipGetLastError();
 }

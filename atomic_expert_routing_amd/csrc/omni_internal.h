@@ -121,6 +121,19 @@ __device__ __forceinline__ float ord_float(unsigned int u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
+// ----------------------------------------------------------------- run gates
+// A launch that may be skipped on the device: the kernel returns at once
+// unless *flag == want (flag == nullptr: always runs).  Used where the
+// choice between two launch sequences is made by an earlier kernel, so the
+// host never waits for it.
+struct RunGate {
+  const int32_t* flag = nullptr;
+  int want = 0;
+};
+__device__ __forceinline__ bool gated_out(const int32_t* flag, int want) {
+  return flag && __builtin_amdgcn_readfirstlane(*flag) != want;
+}
+
 // ----------------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments are pre-validated.
 
@@ -168,7 +181,8 @@ SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 // The sorted group ids left in the workspace by the last launch_schedule.
 const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s,
+                           RunGate run = {});
 // order[0..M) = 0..M-1 stably sorted by keys[i] in [0, key_bound); workspace
 // plan_schedule(M, 1, key_bound, 1).ws_bytes
 hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
@@ -177,7 +191,7 @@ hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32
 // token's first expert); uses the schedule's workspace (plan_schedule(L, K, ..)
 // covers it)
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
-                              int32_t* order, void* ws, hipStream_t s);
+                              int32_t* order, void* ws, hipStream_t s, RunGate gate = {});
 
 // act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order, in
 // chunks along the group boundaries of group_off (B experts per group, G
@@ -186,7 +200,7 @@ int expert_act_chunks(int64_t M);
 hipError_t launch_expert_act(const void* x, const void* W, const int32_t* idx, const float* gate,
                              const int32_t* perm, const int32_t* group_off, int L, int d, int K,
                              int B, int G, omni_dtype dt, float* act, int32_t* start,
-                             hipStream_t s);
+                             hipStream_t s, RunGate run = {});
 // token-centric baseline: y[t] = sum_k gate * SiLU(x_t . W[e]) * V[e], one token per workgroup
 hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const int32_t* idx,
                             const float* gate, int L, int d, int K, omni_dtype dt, float* y,
@@ -195,7 +209,7 @@ hipError_t launch_expert_tc(const void* x, const void* W, const void* V, const i
 // permutation of [0, L), XCD x taking its x-th eighth) or, if null, by id
 hipError_t launch_expert_out(const void* V, const int32_t* idx, const float* act,
                              const int32_t* order, int L, int d, int K, omni_dtype dt, float* y,
-                             hipStream_t s);
+                             hipStream_t s, RunGate run = {});
 
 // ----------------------------------------------------------------- blocked assembly
 constexpr int BLK_TOKENS = 64;       // tokens per block (consecutive entries of the order)
@@ -211,7 +225,31 @@ BlockedPlan plan_blocked(int64_t L, int64_t K, int64_t N);
 // each block of 64 consecutive order entries and the union of their experts
 hipError_t launch_expert_blocked(const void* x, const void* W, const void* V, const int32_t* idx,
                                  const float* gate, const int32_t* order, int L, int d, int K,
-                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s);
+                                 float* y, const BlockedPlan& p, void* ws, hipStream_t s,
+                                 RunGate run = {});
+
+// The schedule and the per-task passes, or the token order and the blocked
+// assembly, chosen on the device from a sample of the routing (see
+// assembly.hip); ws per plan_expert_auto.
+struct AutoPlan {
+  BlockedPlan blk;
+  SchedPlan sched, order_sort;
+  bool blocked_ok;  // bf16, d a multiple of BLK_D_TILE, L small enough
+  int G, sample;    // groups; tasks the choice samples
+  size_t off_flag, off_bits, off_perm, off_goff, off_act, off_start, off_order, off_blk;
+  size_t ws_bytes;
+};
+AutoPlan plan_expert_auto(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B, omni_dtype dt);
+hipError_t launch_expert_auto(const void* x, const void* W, const void* V, const int32_t* idx,
+                              const float* gate, int L, int d, int64_t N, int K, int B,
+                              omni_dtype dt, float* y, int32_t* chosen, const AutoPlan& p,
+                              void* ws, hipStream_t s);
+
+// ----------------------------------------------------------------- measurement aid
+// sink needs gather_probe_blocks(n) * 256 floats
+int gather_probe_blocks(int64_t n);
+hipError_t launch_gather_probe(const void* A, int64_t nA, const int32_t* rows, int64_t n,
+                               int row_bytes, float* sink, hipStream_t s);
 
 // ----------------------------------------------------------------- dense router
 constexpr int DENSE_ROUTER_CHUNK = 65536;  // experts per logits chunk

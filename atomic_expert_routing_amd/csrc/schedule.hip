@@ -44,7 +44,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __res
                                                             const int32_t* __restrict__ keys_in,
                                                             int M, int stride, int B, int shift,
                                                             int radix, int rounds,
-                                                            int ntiles, int* __restrict__ hist) {
+                                                            int ntiles, int* __restrict__ hist,
+                                                            const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int h[256];
   const int tid = threadIdx.x, tile = blockIdx.x;
   if (tid < radix) h[tid] = 0;
@@ -63,7 +65,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_hist(const int32_t* __res
 // stores the digit's total.
 __global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(int* __restrict__ hist,
                                                                    int ntiles,
-                                                                   int* __restrict__ totals) {
+                                                                   int* __restrict__ totals,
+                                                                   const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int wsum[SCHED_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* row = hist + (size_t)blockIdx.x * ntiles;
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
     const int32_t* __restrict__ vals_in, int M, int stride, int B, int shift, int radix,
     int rounds, int ntiles,
     const int* __restrict__ hist, const int* __restrict__ totals, int32_t* __restrict__ keys_out,
-    int32_t* __restrict__ vals_out) {
+    int32_t* __restrict__ vals_out, const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int run[256];
   __shared__ int wcnt[SCHED_THREADS / 64][256];
   const int tid = threadIdx.x, tile = blockIdx.x;
@@ -176,7 +181,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scatter(
 // clustered routing the runs of unused ids reach thousands: one lane
 // writing them took 108 us).
 __global__ __launch_bounds__(256) void sched_offsets(const int32_t* __restrict__ keys, int M,
-                                                     int G, int32_t* __restrict__ off) {
+                                                     int G, int32_t* __restrict__ off,
+                                                     const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   const int p = blockIdx.x * blockDim.x + threadIdx.x, lane = threadIdx.x & 63;
   // ids outside [0, N) break the precondition; clamping keeps the writes in
   // bounds (the offsets are then meaningless, but nothing is corrupted)
@@ -237,7 +244,7 @@ namespace {
 // last pass writes the element indices in sorted order to `vals_last` and
 // leaves the sorted keys in the workspace.
 void sort_by_group(const int32_t* idx, int stride, int M, int B, const SchedPlan& plan,
-                   int32_t* vals_last, void* ws, hipStream_t s) {
+                   int32_t* vals_last, void* ws, hipStream_t s, RunGate run = {}) {
   char* w = (char*)ws;
   int32_t* ka = (int32_t*)(w + plan.off_keys_a);
   int32_t* va = (int32_t*)(w + plan.off_vals_a);
@@ -254,12 +261,12 @@ void sort_by_group(const int32_t* idx, int stride, int M, int B, const SchedPlan
     int32_t* vout = last ? vals_last : ((pass & 1) ? vb : va);
     const int shift = pass * plan.digit_bits;
     hipLaunchKernelGGL(sched_hist, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, M,
-                       stride, B, shift, radix, plan.rounds, plan.ntiles, hist);
+                       stride, B, shift, radix, plan.rounds, plan.ntiles, hist, run.flag, run.want);
     hipLaunchKernelGGL(sched_scan_digits, dim3(radix), dim3(SCHED_THREADS), 0, s, hist,
-                       plan.ntiles, totals);
+                       plan.ntiles, totals, run.flag, run.want);
     hipLaunchKernelGGL(sched_scatter, dim3(plan.ntiles), dim3(SCHED_THREADS), 0, s, idx, kin, vin,
                        M, stride, B, shift, radix, plan.rounds, plan.ntiles, hist, totals, kout,
-                       vout);
+                       vout, run.flag, run.want);
     kin = kout;
     vin = vout;
   }
@@ -268,10 +275,11 @@ void sort_by_group(const int32_t* idx, int stride, int M, int B, const SchedPlan
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
-  sort_by_group(idx, 1, M, B, plan, perm, ws, s);
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s,
+                           RunGate run) {
+  sort_by_group(idx, 1, M, B, plan, perm, ws, s, run);
   hipLaunchKernelGGL(sched_offsets, dim3((M + 1 + 255) / 256), dim3(256), 0, s,
-                     schedule_sorted_keys(plan, ws), M, G, group_off);
+                     schedule_sorted_keys(plan, ws), M, G, group_off, run.flag, run.want);
   return hipGetLastError();
 }
 
@@ -283,10 +291,10 @@ hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32
 }
 
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
-                              int32_t* order, void* ws, hipStream_t s) {
+                              int32_t* order, void* ws, hipStream_t s, RunGate run) {
   // the plan for L elements needs no more workspace than the one for L*K
   const SchedPlan plan = plan_schedule(L, 1, N, B);
-  sort_by_group(idx, K, L, B, plan, order, ws, s);
+  sort_by_group(idx, K, L, B, plan, order, ws, s, run);
   return hipGetLastError();
 }
 

@@ -23,10 +23,13 @@ OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
 OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED, OMNI_OP_EXPERT_BACKWARD_BLOCKED = 6, 7, 8
-EXPORTED = ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_blocked",
+OMNI_OP_EXPERT_FORWARD_AUTO = 9
+EXPORTED = ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_auto",
+            "omni_expert_forward_blocked",
             "omni_expert_backward_blocked",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
-            "omni_shared_mlp", "omni_dense_router", "omni_workspace_bytes", "omni_status_string",
+            "omni_shared_mlp", "omni_dense_router", "omni_gather_probe", "omni_workspace_bytes",
+            "omni_status_string",
             "omni_last_error", "omni_abi_version")
 
 
@@ -56,6 +59,8 @@ def library() -> ctypes.CDLL:
     lib.omni_schedule_noalloc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp]
     lib.omni_expert_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         i64, ctypes.c_int, vp, vp, sz, vp]
+    lib.omni_expert_forward_auto.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                             ctypes.c_int, vp, vp, vp, sz, vp]
     lib.omni_expert_forward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                 ctypes.c_int, vp, vp, sz, vp]
     lib.omni_expert_forward_token_centric.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -72,13 +77,15 @@ def library() -> ctypes.CDLL:
                                     ctypes.c_int, vp, sz, vp]
     lib.omni_dense_router.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
                                       sz, vp]
+    lib.omni_gather_probe.argtypes = [vp, i64, i64, vp, i64, vp, sz, vp]
     lib.omni_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, ctypes.POINTER(sz)]
-    for f in ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_blocked",
+    for f in ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward",
+              "omni_expert_forward_auto", "omni_expert_forward_blocked",
               "omni_expert_backward_blocked",
               "omni_expert_forward_token_centric", "omni_expert_backward",
               "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
-              "omni_workspace_bytes"):
+              "omni_gather_probe", "omni_workspace_bytes"):
         getattr(lib, f).restype = ctypes.c_int
     lib.omni_status_string.argtypes = [ctypes.c_int]
     lib.omni_status_string.restype = ctypes.c_char_p
@@ -249,6 +256,30 @@ def omni_expert_forward(x, W, V, idx, gate, perm, group_off, B: int, y=None, ws=
     return y
 
 
+def omni_expert_forward_auto(x, W, V, idx, gate, B: int, y=None, ws=None, stream=None,
+                             chosen=None):
+    """Schedule and assembly in the form the device picks from a sample of the
+    routing (the pages' schedule and the per-task passes, or the token order
+    and the blocked form when the sampled tasks repeat their experts twice or
+    more) -> y [L, d] float32.  chosen (optional [1] int32) receives 1 when
+    the blocked form ran, else 0."""
+    L, d = x.shape
+    N = W.shape[0]
+    K = idx.shape[1]
+    dt = _dtype_code(x)
+    args = (_dev(x, "x"), _dev(W, "W", x.dtype, (N, d)), _dev(V, "V", x.dtype, (N, d)),
+            _dev(idx, "idx", torch.int32, (L, K)), _dev(gate, "gate", torch.float32, (L, K)))
+    y = torch.empty((L, d), dtype=torch.float32, device=x.device) if y is None else y
+    py = _dev(y, "y", torch.float32, (L, d))
+    pc = None if chosen is None else _dev(chosen, "chosen", torch.int32, (1,))
+    need = (omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD_AUTO, L, d, 1, 1, K, N, B, dt)
+            if ws is None else 0)
+    pw, nw = _workspace(ws, need, x.device)
+    _check(library().omni_expert_forward_auto(*args, L, d, N, K, B, dt, py, pc, pw, nw,
+                                              _stream(stream)), "omni_expert_forward_auto")
+    return y
+
+
 def omni_expert_forward_blocked(x, W, V, idx, gate, token_order, y=None, ws=None, stream=None):
     """The assembly as dense products over blocks of 64 tokens of token_order
     and the union of their experts -> y [L, d] float32 (bf16 inputs)."""
@@ -406,22 +437,40 @@ def omni_dense_router(x, Wn, K: int, idx=None, score=None, gate=None, ws=None, s
     return idx, score, gate
 
 
+def omni_gather_probe(A, rows, sink=None, stream=None):
+    """Measurement aid: read the listed rows of A (2-D, contiguous) in the
+    assembly's access pattern; returns the checksum sink."""
+    n = rows.numel()
+    row_bytes = A.shape[1] * A.element_size()
+    need = 256 * min(8192, max(1, -(-n // 16)))
+    sink = torch.empty(need, dtype=torch.float32, device=A.device) if sink is None else sink
+    _check(library().omni_gather_probe(_dev(A, "A"), A.shape[0], row_bytes,
+                                       _dev(rows, "rows", torch.int32), n,
+                                       _dev(sink, "sink", torch.float32), sink.numel(),
+                                       _stream(stream)), "omni_gather_probe")
+    return sink
+
+
 class RoutedBranch:
     """Preallocated outputs and workspaces for repeated routed-branch forwards.
 
     One instance per (shape, dtype): `forward(x, Wr, Wc, W, V)` enqueues the
-    three C calls on the current stream and allocates nothing.  With
-    token_order=True the schedule also sorts the tokens by their first
-    expert's group and the output pass follows that order: it pays where
-    tokens pile onto few experts (clustered routing) and costs a little on
-    spread-out routing.  assembly="blocked" replaces the per-task assembly by
-    omni_expert_forward_blocked over that order (dense MFMA products per block
-    of 64 tokens and their experts' union): the choice for clustered routing,
-    far slower than the per-task passes on spread-out routing.
+    three C calls on the current stream and allocates nothing.
+
+    assembly="auto" (the default) runs omni_router then
+    omni_expert_forward_auto: the device picks, per call, the pages' schedule
+    and the per-task passes (spread-out routing) or the token order and the
+    blocked form (routing whose tasks pile onto few experts), and writes its
+    choice to `self.chosen` (1 = blocked); `perm` and `group_off` are not
+    filled in this mode (the schedule stays in the workspace).  assembly="expert_centric" always runs the
+    per-task passes (omni_expert_forward); with token_order=True the schedule
+    also sorts the tokens by their first expert's group and the output pass
+    follows that order.  assembly="blocked" always runs
+    omni_expert_forward_blocked over that order.
     """
 
     def __init__(self, L, d, Nr, Nc, K, B, dtype=torch.bfloat16, device="cuda",
-                 token_order=False, assembly="expert_centric"):
+                 token_order=False, assembly="auto"):
         self.L, self.d, self.Nr, self.Nc, self.K, self.B = L, d, Nr, Nc, K, B
         self.N = Nr * Nc
         self.G = -(-self.N // B)
@@ -434,12 +483,14 @@ class RoutedBranch:
         self.perm = torch.empty((L * K,), dtype=i32, **kw)
         self.group_off = torch.empty((self.G + 1,), dtype=i32, **kw)
         self.y = torch.empty((L, d), dtype=f32, **kw)
-        if assembly not in ("expert_centric", "blocked"):
+        self.chosen = torch.zeros((1,), dtype=i32, **kw)
+        if assembly not in ("auto", "expert_centric", "blocked"):
             raise ValueError(f"unknown assembly {assembly!r}")
         self.assembly = assembly
-        token_order = token_order or assembly == "blocked"  # blocks follow the order
+        token_order = (token_order and assembly == "expert_centric") or assembly == "blocked"
         self.token_order = torch.empty((L,), dtype=i32, **kw) if token_order else None
-        op = OMNI_OP_EXPERT_FORWARD_BLOCKED if assembly == "blocked" else OMNI_OP_EXPERT_FORWARD
+        op = {"auto": OMNI_OP_EXPERT_FORWARD_AUTO, "blocked": OMNI_OP_EXPERT_FORWARD_BLOCKED,
+              "expert_centric": OMNI_OP_EXPERT_FORWARD}[assembly]
         sizes = [omni_workspace_bytes(OMNI_OP_ROUTER, L, d, Nr, Nc, K, self.N, B, dt),
                  omni_workspace_bytes(OMNI_OP_SCHEDULE, L, d, Nr, Nc, K, self.N, B, dt),
                  omni_workspace_bytes(op, L, d, Nr, Nc, K, self.N, B, dt)]
@@ -450,11 +501,17 @@ class RoutedBranch:
         return omni_router(x, Wr, Wc, self.K, self.idx, self.score, self.gate, self.ws, stream)
 
     def schedule(self, stream=None):
-        # the blocked assembly reads only the token order
+        # the automatic assembly schedules inside its own call (in the form it
+        # picks); the blocked assembly reads only the token order
+        if self.assembly == "auto":
+            return None
         return omni_schedule(self.idx, self.N, self.B, self.perm, self.group_off, self.ws, stream,
                              self.token_order, tasks=self.assembly != "blocked")
 
     def expert_forward(self, x, W, V, stream=None):
+        if self.assembly == "auto":
+            return omni_expert_forward_auto(x, W, V, self.idx, self.gate, self.B, self.y,
+                                            self.ws, stream, self.chosen)
         if self.assembly == "blocked":
             return omni_expert_forward_blocked(x, W, V, self.idx, self.gate, self.token_order,
                                                self.y, self.ws, stream)

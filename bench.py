@@ -9,26 +9,24 @@ already resident in HBM.  The default workload is 4096 tokens over 1.7M
 atomic experts (d = 2048, N_r = N_c = 1304, K = B = 128, bf16 inputs, fp32
 arithmetic).  Prints ONE JSON line.
 
-Timing: W untimed steps, then exactly K steps between two device
-synchronisations (wall clock), with HIP events (torch.cuda.Event on the
-stream the library launches on) around each call for the per-stage split.
-Then a second branch on a second stream runs alternate steps (two batches
-in flight, each step the whole path on its own buffers), reported as
-two_stream_ms_per_step: one step's router and schedule overlap the other's
-assembly.  It is a throughput figure beside the value, not the value.
-Then the same step is captured once as a HIP graph (the three calls'
-kernels, on preallocated buffers) and W + K replays are timed the same way
-(graph_ms_per_step; --graph makes it the value).  Measured on MI355X the
-replays are about 1.5% slower than eager launches, which already keep the
-GPU busy, so the eager rate is the value by default.
-The roofline entry covers the expert-assembly call (its two kernels:
-expert_act and expert_out_w), whose algorithmic bytes are the unique W and V
-rows gathered, x read once, y written once and 12 bytes of task metadata
-per task; the unique expert count is taken from the step's own ids.
-After the timed steps, --cold-steps more steps each follow a 512 MiB device
-fill that evicts the 256 MB Infinity Cache; their per-stage medians are
-reported as cold_cache_ms_median (the timed value is the warm, back-to-back
-rate).
+Timing: W untimed steps, then exactly K timed steps between two device
+synchronisations, each step after a cache flush (a 1 GiB read, which leaves
+every L2 and the 256 MB Infinity Cache holding clean, unrelated lines), with
+HIP events (torch.cuda.Event on the stream the library launches on) around
+each call.  The value is the mean of those K cold steps.  The same step run
+K times back to back (warm caches) is reported beside it, as are two
+batches in flight on two streams (one step's router and schedule overlap
+the other's assembly; a throughput figure, not the value) and replays of the
+step captured as a HIP graph.
+The assembly is the one RoutedBranch runs by default (--assembly auto): the
+device picks the per-task passes or the blocked form from the routing's
+reuse; config.assembly_chosen says which ran.  The roofline entry covers the
+assembly call: for the per-task passes its algorithmic bytes are the unique
+W and V rows gathered, x read once, y written once and 12 bytes of task
+metadata per task (the unique expert count is taken from the step's own
+ids); for the blocked form it is the executed MFMA work.  The line also
+carries the measured ceilings of this GPU for the assembly's access pattern
+(a random gather of the step's own V rows) and for a device copy.
 
 cpu_baseline: the float64 CPU oracle timed on this host on a bounded sample
 of the same workload's tokens, scaled to the full token count.
@@ -62,19 +60,14 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
                     help="tokens the CPU oracle routes and assembles (capped at L)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="extra steps, each after a 512 MiB write that evicts the 256 MB "
-                         "Infinity Cache, timed with events (0 to skip)")
-    ap.add_argument("--graph", action="store_true",
-                    help="report replays of the step captured as a HIP graph as the value "
-                         "(both rates are always given)")
     ap.add_argument("--no-dense-router", action="store_true",
                     help="skip timing the fully connected router of the ablation")
     ap.add_argument("--token-order", action="store_true",
                     help="time the step with the token-ordered output pass as the headline")
-    ap.add_argument("--assembly", choices=("expert_centric", "blocked"), default="expert_centric",
-                    help="assembly of the headline step (blocked: dense products per token "
-                         "block, for clustered routing)")
+    ap.add_argument("--assembly", choices=("auto", "expert_centric", "blocked"), default="auto",
+                    help="assembly of the headline step: auto (the device picks per call, "
+                         "RoutedBranch's default), expert_centric (the per-task passes) or "
+                         "blocked (dense products per token block)")
     ap.add_argument("--no-two-stream", action="store_true",
                     help="skip the two-batch, two-stream throughput measurement (profiling runs "
                          "use it so that kernel durations are not measured while two steps "
@@ -95,9 +88,10 @@ ASSEMBLY_SRC = os.path.join(ROOT, "atomic_expert_routing_amd", "csrc", "assembly
 PROFILE = os.path.join(ROOT, "profiles", "routed_forward_L4096_N1700416_d2048.md")
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, assembly):
     """Counter-measured bytes per assembly call from the committed rocprofv3
-    summary, or None when it was taken on other kernel source or workload."""
+    summary, or None when it was taken on other kernel source, another
+    workload or another assembly."""
     import hashlib
     import re
 
@@ -105,7 +99,7 @@ def measured_traffic(workload_name):
         return None
     text = open(PROFILE).read()
     m_hash = re.search(r"assembly\.hip sha256: ([0-9a-f]{64})", text)
-    m_bytes = re.search(r"assembly call traffic bytes: (\d+)", text)
+    m_bytes = re.search(r"assembly call traffic bytes \(%s\): (\d+)" % assembly, text)
     if not (m_hash and m_bytes):
         return None
     if hashlib.sha256(open(ASSEMBLY_SRC, "rb").read()).hexdigest() != m_hash.group(1):
@@ -232,13 +226,13 @@ def time_dense_router(inp, w, router_ms, seed, reps=3):
                     "LogSoftmax over N; the pages report 30.6x latency for this substitution"}
 
 
-def blocked_roofline(br, w, mean_ms):
+def blocked_roofline(br, w, mean_ms, order):
     """The blocked assembly's MFMA work: per block of 64 tokens, 64 x npad x d
     products on the W side and twice that on the V side (hi and lo terms),
     npad = the block's union size rounded up to whole 128-column tiles."""
     import torch
 
-    order = br.token_order.long()
+    order = order.long()
     npad = 0
     for b0 in range(0, w.L, 64):
         u = int(torch.unique(br.idx[order[b0:b0 + 64]]).numel())
@@ -253,11 +247,11 @@ def blocked_roofline(br, w, mean_ms):
             "mean_ms": round(mean_ms, 4)}
 
 
-def time_variant(inp, w, br, steps, token_order, assembly="expert_centric"):
-    """Another configuration of the step timed on the same inputs: per-stage
-    medians, and how its y compares with the headline step's (bitwise for
-    the token order alone, whose sums keep their k order; to fp32 rounding
-    for the blocked assembly)."""
+def time_variant(inp, w, br, steps, token_order, assembly, flush):
+    """Another configuration of the step timed on the same inputs, cold as
+    the value: per-stage medians, and how its y compares with the headline
+    step's (bitwise where the same sums are taken in the same order; to fp32
+    rounding otherwise)."""
     import torch
 
     from atomic_expert_routing_amd import omni
@@ -269,6 +263,7 @@ def time_variant(inp, w, br, steps, token_order, assembly="expert_centric"):
     torch.cuda.synchronize()
     evs = []
     for _ in range(steps):
+        flush()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
         bo.router(inp["x"], inp["Wr"], inp["Wc"])
@@ -438,20 +433,40 @@ def main():
         del src, dst
         log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + written")
 
+    # cache flush between cold steps: a 1 GiB read evicts every L2 and the
+    # 256 MB Infinity Cache with clean lines (no write-back left for the step)
+    flush_src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_src.sum()
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # the value: exactly K steps, each after a flush; the events bracket the
+    # step alone, the flushes between them are not counted
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} eager steps")
+    log(f"[bench] timing {args.steps} cold-cache steps")
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush()
+        step(evs[i])
+    torch.cuda.synchronize()
+    cold_ms = statistics.fmean(e[0].elapsed_time(e[3]) for e in evs)
+    # warm: K steps back to back between two synchronisations (wall clock)
+    log(f"[bench] timing {args.steps} warm steps")
+    evs_w = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs_w[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms_step = eager_ms
+    ms_step = cold_ms
+    chosen = (int(br.chosen.item()) if args.assembly == "auto"
+              else int(args.assembly == "blocked"))
     # two batches in flight: a second branch (own outputs and workspace) on a
     # second stream, steps alternating between the two; each step does the
     # whole path, and the two streams overlap one step's router and schedule
@@ -486,7 +501,7 @@ def main():
         two_stream_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         two_stream_same_y = bool(torch.equal(br.y, br2.y))
     del br2, pair
-    # the same step captured once as a HIP graph and replayed
+    # the same step captured once as a HIP graph and replayed (warm)
     br.capture(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     for _ in range(args.warmup):
         br.replay()
@@ -497,19 +512,18 @@ def main():
         br.replay()
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    if args.graph:
-        ms_step = graph_ms
 
-    def med(a, b):
-        return statistics.median(e[a].elapsed_time(e[b]) for e in evs)
+    def med(ev, a, b):
+        return statistics.median(e[a].elapsed_time(e[b]) for e in ev)
 
-    router_ms, sched_ms, expert_ms = med(0, 1), med(1, 2), med(2, 3)
+    router_ms, sched_ms, expert_ms = med(evs, 0, 1), med(evs, 1, 2), med(evs, 2, 3)
     step_min_ms = min(e[0].elapsed_time(e[3]) for e in evs)
     expert_mean_ms = statistics.fmean(e[2].elapsed_time(e[3]) for e in evs)
-    step_ev_ms = med(0, 3)
+    step_ev_ms = med(evs, 0, 3)
 
-    # algorithmic bytes of one expert-assembly call (one launch of the pair)
-    U = int(torch.unique(br.idx).numel())
+    # algorithmic bytes of one expert-assembly call (the per-task passes)
+    uniq = torch.unique(br.idx)
+    U = int(uniq.numel())
     es = 2 if w.dtype == "bf16" else 4
     expert_bytes = U * 2 * w.d * es + w.L * w.d * es + w.L * w.d * 4 + w.M * 12
     achieved = expert_bytes / (expert_mean_ms * 1e-3) / 1e9
@@ -517,6 +531,59 @@ def main():
     sched_bytes = w.M * 4 + w.M * 4 + (w.G + 1) * 4
     branch_bytes = expert_bytes + router_bytes + sched_bytes
     router_flops = 2.0 * w.L * w.d * (w.Nr + w.Nc)
+
+    # measured ceilings: the step's own V rows gathered in random order (the
+    # assembly's access pattern), cold; and a 1 GiB device copy
+    log("[bench] ceilings: row gather and copy")
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 11)
+    rows = uniq[torch.randperm(U, generator=g, device="cuda")].to(torch.int32).contiguous()
+    sink = omni.omni_gather_probe(inp["V"], rows)
+    gather_t = []
+    for _ in range(5):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        omni.omni_gather_probe(inp["V"], rows, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gather_t.append(e0.elapsed_time(e1))
+    gather_gbs = U * w.d * es / (statistics.median(gather_t) * 1e-3) / 1e9
+    cdst = torch.empty_like(flush_src)
+    copy_t = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cdst.copy_(flush_src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_t.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * flush_src.numel() / (statistics.median(copy_t) * 1e-3) / 1e9
+    del cdst, sink
+
+    if chosen:
+        order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True, tasks=False)[2]
+        roofline = blocked_roofline(br, w, expert_mean_ms, order)
+        roofline["kernel"] = ("omni_expert_forward_auto, blocked form chosen (auto_clear, "
+                              "auto_mark, auto_choose, token order sort, blk_union, blk_plan, "
+                              "blk_act, blk_out)" if args.assembly == "auto" else roofline["kernel"])
+    else:
+        roofline = {
+            "kernel": ("omni_expert_forward_auto, schedule and per-task passes chosen "
+                       "(auto_clear, auto_mark, auto_choose, the schedule's radix sort and "
+                       "sched_offsets, act_plan, expert_act, expert_out_w)"
+                       if args.assembly == "auto"
+                       else "omni_expert_forward (act_plan, expert_act, expert_out_w)"),
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, args.assembly),
+            "algorithmic_bytes": expert_bytes,
+            "mean_ms": round(expert_mean_ms, 4),
+            "ceiling_row_gather_GBs": round(gather_gbs, 1),
+            "frac_of_row_gather_ceiling": round(achieved / gather_gbs, 4),
+        }
 
     out = {
         "metric": METRIC,
@@ -533,74 +600,58 @@ def main():
         "data": "synthetic: seeded Gaussian x and random-init W, V, W_r, W_c (no trained weights)",
         "config": {**w.describe(), "parallelism": "single GPU",
                    "token_ordered_output": bool(args.token_order or args.assembly == "blocked"),
-                   "assembly": args.assembly},
+                   "assembly": args.assembly,
+                   "assembly_chosen": "blocked" if chosen else "per_task"},
         "tokens_per_s": round(w.L / (ms_step * 1e-3), 1),
-        "timing": "replays of the step captured as a HIP graph" if args.graph
-                  else "eager launches",
-        "eager_ms_per_step": round(eager_ms, 4),
+        "timing": "mean of the K timed steps, each after a cache flush (cold); events around "
+                  "the step",
+        "warm_ms_per_step": round(eager_ms, 4),
         "graph_ms_per_step": round(graph_ms, 4),
         "two_stream_ms_per_step": None if two_stream_ms is None else round(two_stream_ms, 4),
         "two_stream_note": "throughput with two independent batches in flight on two streams "
-                           "(each step the whole path on its own buffers); not the value",
+                           "(each step the whole path on its own buffers, warm); not the value",
         "two_stream_y_bitwise_equal": two_stream_same_y,
         "branch_hbm_frac": round(branch_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "stages_ms_median": {"router": round(router_ms, 4), "schedule": round(sched_ms, 4),
                              "expert_forward": round(expert_ms, 4),
                              "step_events": round(step_ev_ms, 4)},
+        "warm_stages_ms_median": {"router": round(med(evs_w, 0, 1), 4),
+                                  "schedule": round(med(evs_w, 1, 2), 4),
+                                  "expert_forward": round(med(evs_w, 2, 3), 4),
+                                  "step_events": round(med(evs_w, 0, 3), 4)},
         "unique_experts": U,
-        "roofline": {
-            "kernel": "omni_expert_forward (expert_act + expert_out_w)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
-            "algorithmic_bytes": expert_bytes,
-            "mean_ms": round(expert_mean_ms, 4),
-        } if args.assembly == "expert_centric" else blocked_roofline(br, w, expert_mean_ms),
+        "roofline": roofline,
+        "ceilings": {"row_gather_GBs": round(gather_gbs, 1), "copy_GBs": round(copy_gbs, 1),
+                     "note": "row gather: the step's unique V rows read once in random order, "
+                             "one wave per row, after a flush (omni_gather_probe); copy: a "
+                             "1 GiB device copy, bytes read plus written"},
         "router_gemm_flops": router_flops,
     }
-    # cold cache: before each of these steps a 512 MiB fill evicts the 256 MB
-    # Infinity Cache (and every L2); the events bracket the step alone
-    if args.cold_steps:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cold = []
-        for _ in range(args.cold_steps):
-            flush.fill_(1)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            step(ev)
-            torch.cuda.synchronize()
-            cold.append([ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
-                         ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[3])])
-        del flush
-        cm = [statistics.median(c[i] for c in cold) for i in range(4)]
-        out["cold_cache_ms_median"] = {"router": round(cm[0], 4), "schedule": round(cm[1], 4),
-                                       "expert_forward": round(cm[2], 4), "step": round(cm[3], 4)}
     out["step_events_ms_min"] = round(step_min_ms, 4)
 
     # the token-centric order the expert-centric schedule replaces, timed on
-    # the same routing (same y up to rounding)
+    # the same routing (same y up to rounding), cold as the value
     tc_times = []
     y_tc = torch.empty_like(br.y)
-    for i in range(args.steps + 2):
+    omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate, y_tc)
+    for i in range(args.steps):
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate, y_tc)
         e1.record()
         torch.cuda.synchronize()
-        if i >= 2:
-            tc_times.append(e0.elapsed_time(e1))
+        tc_times.append(e0.elapsed_time(e1))
     tc_ms = statistics.median(tc_times)
     out["token_centric_assembly_ms"] = round(tc_ms, 4)
     out["expert_centric_speedup_vs_token_centric"] = round(tc_ms / expert_ms, 3)
 
     variants = []
-    if args.assembly == "expert_centric":
-        variants.append(time_variant(inp, w, br, args.steps, not args.token_order))
-    if w.dtype == "bf16" and w.d % 256 == 0:
-        variants.append(time_variant(inp, w, br, args.steps, True,
-                                     "expert_centric" if args.assembly == "blocked" else "blocked"))
+    if args.assembly != "expert_centric":
+        variants.append(time_variant(inp, w, br, args.steps, False, "expert_centric", flush))
+    variants.append(time_variant(inp, w, br, args.steps, True, "expert_centric", flush))
+    if w.dtype == "bf16" and w.d % 256 == 0 and args.assembly != "blocked":
+        variants.append(time_variant(inp, w, br, args.steps, True, "blocked", flush))
     out["variants"] = variants
 
     out["shared_mlp"] = time_mlp(inp, w, args.steps, args.seed, step_ev_ms)

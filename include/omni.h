@@ -7,6 +7,8 @@
  *   omni_router          Cartesian Product Router: ids, scores, gates
  *   omni_schedule        expert-centric schedule: sorted tasks, group offsets
  *   omni_expert_forward  Dynamic Expert Assembly: y
+ * or in two, with the schedule and the assembly in the form the device picks
+ * for the routing: omni_router, then omni_expert_forward_auto.
  * with a dense variant of the assembly for routing in which many tokens share
  * experts, omni_expert_forward_blocked, and one comparison baseline,
  * omni_expert_forward_token_centric.
@@ -75,7 +77,8 @@ typedef enum {
   OMNI_OP_SHARED_MLP = 5, /* omni_workspace_bytes takes d_ff in its N argument */
   OMNI_OP_DENSE_ROUTER = 6,
   OMNI_OP_EXPERT_FORWARD_BLOCKED = 7,
-  OMNI_OP_EXPERT_BACKWARD_BLOCKED = 8
+  OMNI_OP_EXPERT_BACKWARD_BLOCKED = 8,
+  OMNI_OP_EXPERT_FORWARD_AUTO = 9
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -260,6 +263,42 @@ OMNI_API omni_status omni_expert_forward_blocked(const void* x, const void* W, c
                                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * omni_expert_forward_auto - the expert-centric schedule and assembly, in the
+ * form that suits the step's routing, chosen on the device per call (the
+ * host never waits).
+ * Source: the schedule and assembly of omni_schedule and omni_expert_forward
+ * (OmniMoE digest, method paragraph, steps 1 and 3); the choice answers the
+ * digest's weaknesses paragraph, which names grouping efficiency under
+ * changing active-expert sets as the open problem of expert-centric
+ * scheduling.
+ *
+ * A first kernel counts the distinct experts among a fixed sample of the
+ * tasks (all L*K tasks when there are at most 65536, else tasks
+ * i * 2654435761 mod L*K for i < 65536).  When the sample repeats its
+ * experts twice or more on average, the blocked form runs: the token order
+ * (as omni_schedule's token_order), then omni_expert_forward_blocked over it.
+ * Otherwise the pages' schedule runs (perm and group_off with group size B,
+ * as omni_schedule, kept in the workspace) and then the per-task passes of
+ * omni_expert_forward.  The launches of the form not chosen return at once.
+ * y is the same up to the rounding of the form taken (see
+ * omni_expert_forward_blocked).  The blocked form is only considered for
+ * bf16 inputs with d % 256 == 0.
+ *
+ *   x, W, V, idx, gate, B, y   as for omni_expert_forward
+ *   chosen  [1] int32 out, optional (NULL: not written): 1 when the blocked
+ *           form ran, 0 for the schedule and the per-task passes
+ * Requires what omni_schedule and omni_expert_forward require, and the K ids
+ * of each token distinct (as omni_router returns them).  Workspace
+ * (omni_workspace_bytes(OMNI_OP_EXPERT_FORWARD_AUTO, ..., B, ...)): the
+ * choice, a bitmap of N bits, and the larger of the two forms' buffers.
+ */
+OMNI_API omni_status omni_expert_forward_auto(const void* x, const void* W, const void* V,
+                                              const int32_t* idx, const float* gate, int64_t L,
+                                              int64_t d, int64_t N, int64_t K, int64_t B,
+                                              omni_dtype dt, float* y, int32_t* chosen,
+                                              void* ws, size_t ws_bytes, void* stream);
+
+/*
  * omni_expert_forward_token_centric - the same y as omni_expert_forward,
  * computed in token-centric order: each token fetches the W and V rows of
  * its own K experts, with no schedule.  This is the execution order that the
@@ -429,6 +468,21 @@ OMNI_API omni_status omni_dense_router(const void* x, const void* Wn, int64_t L,
                                        int64_t N, int64_t K, omni_dtype dt, int32_t* idx,
                                        float* score, float* gate, void* ws, size_t ws_bytes,
                                        void* stream);
+
+/*
+ * omni_gather_probe - measurement aid, not part of the method: reads the
+ * listed rows of a row-major matrix A [n_rows_A, row_bytes] in random order
+ * (one wave per row, four rows in flight), as the expert assembly reads the
+ * rows of W and V, and writes a checksum per thread to sink.  Timed on the
+ * rows a step uses, it gives the gather rate the memory system delivers for
+ * that pattern, beside the nominal HBM peak.
+ *   rows  [n] int32   row ids; ids outside [0, n_rows_A) are skipped
+ *   sink  [sink_floats] fp32 out, at least 256 * min(8192, ceil(n / 16))
+ * Requires row_bytes a multiple of 16 in [16, 65536].
+ */
+OMNI_API omni_status omni_gather_probe(const void* A, int64_t n_rows_A, int64_t row_bytes,
+                                       const int32_t* rows, int64_t n, float* sink,
+                                       size_t sink_floats, void* stream);
 
 /*
  * omni_workspace_bytes - workspace size needed by one call of `op` with

@@ -104,7 +104,7 @@ def test_schedule_validation():
         with pytest.raises(omni.OmniError):
             omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, **args)
     with pytest.raises(omni.OmniError):
-        omni.omni_workspace_bytes(9)
+        omni.omni_workspace_bytes(10)
 
 
 @pytest.mark.parametrize("B", [2**31, 2**32, 2**32 + 5, 2**62])
@@ -315,3 +315,43 @@ def test_noalloc_schedule_rejects_before_touching_the_gpu():
     # the largest configured workload (16384 x 256 tasks) fits
     assert omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, L=16384, K=256, N=1700416,
                                      B=256) <= 80 << 20
+
+
+def test_auto_assembly_workspace_and_validation():
+    """omni_expert_forward_auto: the schedule's and the assembly's size rules,
+    a workspace that holds either form, and rejections before any launch."""
+    L, d, K, N, B = 4096, 2048, 128, 1700416, 128
+    auto = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_AUTO, L=L, d=d, K=K, N=N, B=B)
+    blocked = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_BLOCKED, L=L, d=d, K=K, N=N)
+    per_task = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD, L=L, d=d, K=K, N=N, B=B)
+    assert auto >= blocked and auto >= per_task + L * K * 4
+    # fp32 inputs never take the blocked form: a smaller workspace
+    f32 = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_AUTO, L=L, d=d, K=K, N=N, B=B,
+                                    dtype=omni.OMNI_F32)
+    assert f32 < blocked
+    for kw, st in ((dict(B=0), omni.OMNI_ERR_INVALID_ARG), (dict(B=2**31), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(K=513), omni.OMNI_ERR_UNSUPPORTED), (dict(d=12), omni.OMNI_ERR_UNSUPPORTED)):
+        args = dict(L=64, d=256, K=16, N=1024, B=16)
+        args.update(kw)
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_FORWARD_AUTO, **args)
+        assert e.value.status == st
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)
+    s = lib.omni_expert_forward_auto(fake, fake, fake, None, fake, 64, 256, 1024, 16, 16,
+                                     omni.OMNI_BF16, fake, None, fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
+    s = lib.omni_expert_forward_auto(fake, fake, fake, fake, fake, 64, 256, 1024, 16, 16,
+                                     omni.OMNI_BF16, fake, None, fake, 16, None)
+    assert s == omni.OMNI_ERR_WORKSPACE
+
+
+def test_gather_probe_validation():
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)
+    s = lib.omni_gather_probe(fake, 10, 24, fake, 5, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_UNSUPPORTED  # row bytes not a multiple of 16
+    s = lib.omni_gather_probe(fake, 10, 64, fake, 5, fake, 16, None)
+    assert s == omni.OMNI_ERR_WORKSPACE  # sink too small
+    s = lib.omni_gather_probe(None, 10, 64, fake, 5, fake, 1 << 20, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG

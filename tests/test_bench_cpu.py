@@ -26,14 +26,14 @@ def test_profile_traffic_is_tied_to_the_assembly_source():
     recorded = [ln.split(": ")[1] for ln in text.splitlines() if "assembly.hip sha256" in ln]
     assert len(recorded) == 1
     now = hashlib.sha256(open(bench.ASSEMBLY_SRC, "rb").read()).hexdigest()
-    got = bench.measured_traffic("L4096_N1700416_d2048")
+    got = bench.measured_traffic("L4096_N1700416_d2048", "auto")
     if recorded[0] == now:
         # the counters were taken on this source: the bytes are reported, and
-        # they exceed the algorithmic bytes (every task reads a W and a V row)
+        # they exceed the algorithmic bytes (every task reads a V row)
         assert isinstance(got, int) and got > 3.7e9
     else:
         assert got is None
-    assert bench.measured_traffic("L4096_N280900_d768") is None
+    assert bench.measured_traffic("L4096_N280900_d768", "auto") is None
 
 
 @pytest.mark.parametrize("name", ["L4096_N1700416_d2048"])

@@ -255,7 +255,8 @@ def test_blocked_backward_full_size(name):
     w = synth.WORKLOADS[name]
     say(f"blocked backward full-size {name}")
     inp = synth.make_inputs(w, seed=0, device="cuda")
-    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True)
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True,
+                           assembly="expert_centric")
     br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     dy = synth.upstream_grad(w, seed=0, device="cuda")
     ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy)

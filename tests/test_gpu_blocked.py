@@ -34,7 +34,8 @@ def need_gpu():
 
 def routed(inp, w):
     """Router + schedule with the token order, then the per-task assembly."""
-    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True)
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True,
+                           assembly="expert_centric")
     br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     torch.cuda.synchronize()
     return br

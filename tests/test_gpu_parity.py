@@ -31,8 +31,11 @@ def need_gpu():
     omni.library()  # fails loudly if the HIP library is missing
 
 
-def run_branch(inp, w):
-    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
+def run_branch(inp, w, assembly="expert_centric"):
+    """Router, schedule and assembly through RoutedBranch; the per-task passes
+    unless another assembly is named (the full-size tests run the default,
+    device-chosen one, as the benchmark does)."""
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, assembly=assembly)
     br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
     torch.cuda.synchronize()
     return br
@@ -194,7 +197,8 @@ def test_token_ordered_output_pass(case):
     br = run_branch(inp, w)
     check_token_order(inp, br, w)
     # through RoutedBranch, run twice (the second over a stale y)
-    bo = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True)
+    bo = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype, token_order=True,
+                           assembly="expert_centric")
     for _ in range(2):
         bo.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
         torch.cuda.synchronize()
@@ -264,18 +268,42 @@ LARGE = ["L4096_N280900_d768", "L4096_N1048576_d1024", synth.HEADLINE,
          "skewed_L16384_N1700416_d2048"]
 
 
+def class_sample(L, per_class=8, seed=7):
+    """Tokens 0 and L-1 plus per_class random tokens of each class t % 8 (the
+    activation pass splits its work by that class across the XCDs)."""
+    rs = np.random.Generator(np.random.PCG64(seed))
+    picks = [0, L - 1]
+    for c in range(8):
+        members = np.arange(c, L, 8)
+        picks.extend(rs.choice(members, min(per_class, len(members)), replace=False))
+    return np.unique(np.asarray(picks, np.int64))
+
+
+def check_rows(y, y_ref, rtol):
+    """Row by row: max |y - y_ref| <= rtol * max |y_ref| within each row."""
+    diff = (y - y_ref).abs().amax(dim=1)
+    scale = y_ref.abs().amax(dim=1).clamp_min(1e-30)
+    worst = (diff / scale).max().item()
+    assert worst <= rtol, worst
+    return worst
+
+
 @pytest.mark.parametrize("name", LARGE)
 def test_full_size_workload_sampled(name):
     w = synth.WORKLOADS[name]
     say(f"full-size {name}: generating inputs")
     inp = synth.make_inputs(w, seed=0, device="cuda")
-    say(f"full-size {name}: routed forward")
-    br = run_branch(inp, w)
-    # schedule: whole arrays, bit-exact
+    say(f"full-size {name}: routed forward (default assembly, as the benchmark runs it)")
+    br = run_branch(inp, w, assembly="auto")
+    chosen = int(br.chosen.item())
+    # the device picks the blocked form for the clustered workload only
+    assert chosen == (1 if w.x_dist == "clustered" else 0), chosen
+    # schedule of the same ids (omni_schedule): whole arrays, bit-exact
+    br.perm, br.group_off = omni.omni_schedule(br.idx, w.N, w.B)
+    torch.cuda.synchronize()
     check_schedule(br.idx, br.perm, br.group_off, w.N, w.B)
-    # router and assembly: sampled tokens (first, last and spread)
-    rs = np.random.Generator(np.random.PCG64(7))
-    toks = np.unique(np.concatenate([[0, w.L - 1], rs.choice(w.L, 30, replace=False)]))
+    # router and assembly: 8 sampled tokens of every class t % 8, plus the ends
+    toks = class_sample(w.L)
     xs = to_np(inp["x"][torch.as_tensor(toks, device="cuda")])
     _, _, _, p_r, p_c = O.route(xs, inp["Wr"], inp["Wc"], w.K)
     idx = to_np(br.idx)[toks]
@@ -283,14 +311,27 @@ def test_full_size_workload_sampled(name):
     y_o = O.assemble_token_centric(xs, DeviceRows(inp["W"]), DeviceRows(inp["V"]),
                                    idx, to_np(br.gate)[toks])
     nrm, mx = check_y(to_np(br.y)[toks], y_o, min(RTOL[w.dtype], RTOL_FP32_ARITH))
-    say(f"  swaps={swaps} over {len(toks)} tokens; y_err norm={nrm:.2e} max={mx:.2e}")
-    # token-centric baseline on the same routing, whole y against the method's
+    say(f"  chosen={chosen} swaps={swaps} over {len(toks)} tokens; y_err norm={nrm:.2e} "
+        f"max={mx:.2e}")
+    # the per-task passes on the same routing: the sampled tokens against the
+    # oracle, and the whole y against the token-centric kernel row by row
+    y_pt = omni.omni_expert_forward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, br.perm,
+                                    br.group_off, w.B)
+    torch.cuda.synchronize()
+    check_y(to_np(y_pt)[toks], y_o, min(RTOL[w.dtype], RTOL_FP32_ARITH))
     y_tc = omni.omni_expert_forward_token_centric(inp["x"], inp["W"], inp["V"], br.idx, br.gate)
     torch.cuda.synchronize()
-    dy = (y_tc - br.y).norm() / br.y.norm()
+    dy = (y_tc - y_pt).norm() / y_pt.norm()
     assert dy.item() <= RTOL_FP32_ARITH, dy.item()
+    worst = check_rows(y_tc, y_pt, RTOL_FP32_ARITH)
+    if chosen:
+        check_rows(br.y, y_pt, RTOL_FP32_ARITH)
+    else:
+        assert torch.equal(br.y, y_pt)  # the same kernels ran
+    say(f"  token-centric vs per-task: norm {dy.item():.2e}, worst row {worst:.2e}")
     # token-ordered output pass: the order bit-exact, y bitwise unchanged
     say(f"full-size {name}: token order")
+    br.y.copy_(y_pt)
     check_token_order(inp, br, w)
     del inp, br
     torch.cuda.empty_cache()

@@ -24,7 +24,7 @@ def need_gpu():
 
 CASES = [
     ((512, 256, 40, 36, 32, 16, "bf16"), {}),
-    ((300, 512, 48, 48, 64, 32, "bf16"), {"token_order": True}),
+    ((300, 512, 48, 48, 64, 32, "bf16"), {"token_order": True, "assembly": "expert_centric"}),
     ((128, 64, 32, 32, 16, 16, "f32"), {}),
 ]
 
@@ -44,7 +44,8 @@ def test_two_streams_match_one(case, opts):
         ref = omni.RoutedBranch(L, d, Nr, Nc, K, B, w.torch_dtype, **opts)
         ref.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
         torch.cuda.synchronize()
-        want.append({k: getattr(ref, k).clone() for k in ("idx", "gate", "perm", "group_off", "y")})
+        names = ("idx", "gate", "y") + (("perm", "group_off") if ref.assembly != "auto" else ())
+        want.append({k: getattr(ref, k).clone() for k in names})
     branches = [omni.RoutedBranch(L, d, Nr, Nc, K, B, w.torch_dtype, **opts) for _ in ins]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
     start = torch.cuda.Event()
