@@ -171,11 +171,14 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
                               int32_t* idx, float* score, float* gate, hipStream_t s);
 size_t router_topk_lds_bytes(int Nr, int Nc, int K);
 
+constexpr int GROUP_HIST_MAX = 16384;  // groups the scatter counts in LDS (32 KB)
 struct SchedPlan {
-  int M, G, rounds, ntiles, passes, digit_bits;  // a tile is rounds x 256 elements
+  int M, G, rounds, ntiles, passes, digit_bits;  // a tile is rounds x 1024 elements
+  bool group_hist;  // G <= GROUP_HIST_MAX, M <= 8M: the scatter passes also produce group_off
   size_t ws_bytes;
   // workspace carve (byte offsets)
-  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals;
+  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals, off_gcount,
+      off_ticket;
 };
 SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 // The sorted group ids left in the workspace by the last launch_schedule.
