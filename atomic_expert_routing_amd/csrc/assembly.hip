@@ -142,9 +142,9 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
   const int lane = threadIdx.x;
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int part = blockIdx.x % XCDS;
-  // the gate flag is read together with the first chunk's bounds (one
+  // the gate's words are read together with the first chunk's bounds (one
   // memory latency, not two, before the work starts)
-  const int flag = run_flag ? run_flag[0] : run_want;
+  const int g_distinct = run_flag ? run_flag[1] : 0, g_sampled = run_flag ? run_flag[2] : 0;
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   const unsigned cb = lane * 16u;
   auto load_x = [&](int t, u32x4* r) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
   for (int chunk = blockIdx.x / XCDS; chunk < nchunks; chunk += gridDim.x / XCDS) {
     const int p0 = start[chunk];
     const int n = start[chunk + 1] - p0;  // 0 .. 2*ACT_CHUNK-1
-    if (__builtin_amdgcn_readfirstlane(flag) != run_want) return;
+    if (run_flag && auto_choice_of(g_distinct, g_sampled) != run_want) return;
     const bool v = lane < n;
     const int m = v ? perm[p0 + lane] : 0;
     const bool mine = v && (m / K) % XCDS == part;
@@ -300,13 +300,13 @@ __global__ __launch_bounds__(256) void expert_out_w(const uint16_t* __restrict__
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int t = 4 * blockIdx.x + w;
   if (t >= L) return;  // whole wave; no workgroup barrier follows
-  // the gate flag is read beside the token's ids and activations
-  const int flag = run_flag ? run_flag[0] : run_want;
+  // the gate's words are read beside the token's ids and activations
+  const int g_distinct = run_flag ? run_flag[1] : 0, g_sampled = run_flag ? run_flag[2] : 0;
   for (int k = lane; k < K; k += 64) {
     se[w][k] = idx[(size_t)t * K + k];
     sa[w][k] = act[(size_t)t * K + k];
   }
-  if (__builtin_amdgcn_readfirstlane(flag) != run_want) return;
+  if (run_flag && auto_choice_of(g_distinct, g_sampled) != run_want) return;
   wave_sync();
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   const unsigned cb = lane * 16u;
@@ -502,19 +502,24 @@ hipError_t launch_act_t(const void* x, const void* W, const int32_t* idx, const 
 // them when there are at most AUTO_SAMPLE; else tasks i * 2654435761 mod M,
 // distinct for distinct i) and counts the distinct experts among them, one
 // bit per expert, the count of newly set bits adding up as it goes.
-// auto_choose then sets a flag: the blocked form when the sample holds each
-// of its experts AUTO_REUSE times or more on average.  Every launch of both
-// forms reads the flag and the form not chosen returns at once.  Measured:
-// at 16384 clustered tokens x K = 256 the blocked form takes 0.48 ms
-// against 1.7 ms; on spread-out routing (1.2 to 1.6 tasks per expert) the
-// per-task passes take 0.78 ms against 1.1 ms at 4096 tokens x 1.7M experts.
+// The blocked form is taken when the sample holds each of its experts
+// AUTO_REUSE times or more on average (auto_choice, which every kernel of
+// both forms evaluates from the two counts; the form not chosen returns at
+// once).  The two sorts (the schedule's, over the tasks, and the token order
+// the blocked form follows) share one set of launches.  Measured: at 16384
+// clustered tokens x K = 256 the blocked form takes 0.48 ms against 1.7 ms;
+// on spread-out routing (1.2 to 1.6 tasks per expert) the per-task passes
+// take 0.78 ms against 1.1 ms at 4096 tokens x 1.7M experts.
 constexpr int AUTO_SAMPLE = 65536;
-constexpr int AUTO_REUSE = 2;
 
+// gate[1] = 0 distinct experts so far, gate[2] = the sample size S
 __global__ __launch_bounds__(256) void auto_clear(uint32_t* __restrict__ bits, int nwords,
-                                                  int32_t* __restrict__ counter) {
+                                                  int32_t* __restrict__ gate, int S) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < nwords; i += gridDim.x * 256) bits[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x == 0) counter[0] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    gate[1] = 0;
+    gate[2] = S;
+  }
 }
 
 __global__ __launch_bounds__(256) void auto_mark(const int32_t* __restrict__ idx, int M, int N,
@@ -533,16 +538,6 @@ __global__ __launch_bounds__(256) void auto_mark(const int32_t* __restrict__ idx
   fresh = wave_sum_i(fresh);
   if ((threadIdx.x & 63) == 0 && fresh) atomicAdd(counter, fresh);
 }
-
-__global__ void auto_choose(const int32_t* __restrict__ counter, int S,
-                            int32_t* __restrict__ flag, int32_t* __restrict__ chosen) {
-  const int distinct = counter[0];
-  const int blocked = (int64_t)S >= (int64_t)AUTO_REUSE * distinct ? 1 : 0;
-  flag[0] = blocked;
-  if (chosen) chosen[0] = blocked;
-}
-
-__global__ void auto_set(int32_t* __restrict__ chosen, int v) { chosen[0] = v; }
 
 }  // namespace
 
@@ -614,7 +609,7 @@ AutoPlan plan_expert_auto(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B,
   p.sched = plan_schedule(L, K, N, B);
   p.blocked_ok = dt == OMNI_BF16 && d % BLK_D_TILE == 0 && L <= INT32_MAX - BLK_TOKENS;
   size_t o = 0;
-  p.off_flag = o;   o += 256;  // [0] the choice, [1] distinct experts in the sample
+  p.off_flag = o;   o += 256;  // [1] distinct experts in the sample, [2] the sample size
   p.off_bits = o;   o += a256((size_t)((N + 31) / 32) * 4);
   const size_t base = o;
   // per-task passes: perm, group_off, then the schedule's sort buffers,
@@ -650,34 +645,38 @@ hipError_t launch_expert_auto(const void* x, const void* W, const void* V, const
   int32_t* start = (int32_t*)(w + p.off_start);
   hipError_t e;
   RunGate per_task{}, blocked{};
+  int32_t* choice = nullptr;  // the run gate: [1] distinct experts, [2] sample size
   if (p.blocked_ok) {
-    int32_t* flag = (int32_t*)(w + p.off_flag);
+    choice = (int32_t*)(w + p.off_flag);
     uint32_t* bits = (uint32_t*)(w + p.off_bits);
     const int nwords = (int)((N + 31) / 32);
     hipLaunchKernelGGL(auto_clear, dim3((unsigned)std::min(512, (nwords + 255) / 256)),
-                       dim3(256), 0, s, bits, nwords, flag + 1);
+                       dim3(256), 0, s, bits, nwords, choice, p.sample);
     hipLaunchKernelGGL(auto_mark, dim3((unsigned)((p.sample + 255) / 256)), dim3(256), 0, s, idx,
-                       M, (int)N, p.sample, bits, flag + 1);
-    hipLaunchKernelGGL(auto_choose, dim3(1), dim3(1), 0, s, flag + 1, p.sample, flag, chosen);
-    per_task = RunGate{flag, 0};
-    blocked = RunGate{flag, 1};
-  } else if (chosen) {  // the blocked form cannot take these inputs
-    hipLaunchKernelGGL(auto_set, dim3(1), dim3(1), 0, s, chosen, 0);
+                       M, (int)N, p.sample, bits, choice + 1);
+    per_task = RunGate{choice, 0};
+    blocked = RunGate{choice, 1};
   }
-  // per-task passes: the pages' schedule, then the two passes over it
-  e = launch_schedule(idx, M, B, p.G, p.sched, perm, goff, w + p.off_act, s, per_task);
+  // the sort of the chosen form: the pages' schedule of the tasks for the
+  // per-task passes, the token order for the blocked form (it also writes
+  // `chosen`)
+  const SortSpec tasks{idx, 1, M, B, p.sched, perm, w + p.off_act};
+  const SortSpec tokens =
+      p.blocked_ok ? token_order_spec(idx, L, K, N, B, (int32_t*)(w + p.off_order), w + p.off_blk)
+                   : tasks;
+  e = sort_dual(tasks, tokens, choice, chosen, s);
+  if (e != hipSuccess) return e;
+  // per-task passes: group offsets, then the two passes over the schedule
+  e = launch_sched_offsets(p.sched, w + p.off_act, M, p.G, goff, s, per_task);
   if (e != hipSuccess) return e;
   e = launch_expert_act(x, W, idx, gate, perm, goff, L, d, K, B, p.G, dt, act, start, s,
                         per_task);
   if (e != hipSuccess) return e;
   e = launch_expert_out(V, idx, act, nullptr, L, d, K, dt, y, s, per_task);
   if (e != hipSuccess || !p.blocked_ok) return e;
-  // blocked form: the token order, then the dense products per token block
-  int32_t* order = (int32_t*)(w + p.off_order);
-  e = launch_token_order(idx, L, K, N, B, order, w + p.off_blk, s, blocked);
-  if (e != hipSuccess) return e;
-  return launch_expert_blocked(x, W, V, idx, gate, order, L, d, K, y, p.blk, w + p.off_blk, s,
-                               blocked);
+  // blocked form: the dense products per block of the token order
+  return launch_expert_blocked(x, W, V, idx, gate, (const int32_t*)(w + p.off_order), L, d, K,
+                               y, p.blk, w + p.off_blk, s, blocked);
 }
 
 }  // namespace omni

@@ -122,16 +122,30 @@ __device__ __forceinline__ float ord_float(unsigned int u) {
 }
 
 // ----------------------------------------------------------------- run gates
+// The expert assembly picks its form on the device from a sample of the
+// routing: gate[1] distinct experts among gate[2] sampled tasks (both set by
+// earlier kernels of the same call); the blocked form when each sampled
+// expert is used AUTO_REUSE times or more on average.  Every kernel of either
+// form reads the two words and computes the choice itself, so the host never
+// waits for it and no launch is spent on deciding.
+constexpr int AUTO_REUSE = 2;
+__device__ __forceinline__ int auto_choice_of(int distinct, int sampled) {
+  distinct = __builtin_amdgcn_readfirstlane(distinct);
+  sampled = __builtin_amdgcn_readfirstlane(sampled);
+  return (int64_t)sampled >= (int64_t)AUTO_REUSE * distinct ? 1 : 0;
+}
+__device__ __forceinline__ int auto_choice(const int32_t* gate) {
+  return auto_choice_of(gate[1], gate[2]);
+}
 // A launch that may be skipped on the device: the kernel returns at once
-// unless *flag == want (flag == nullptr: always runs).  Used where the
-// choice between two launch sequences is made by an earlier kernel, so the
-// host never waits for it.
+// unless the choice read from `flag` equals want (flag == nullptr: always
+// runs).
 struct RunGate {
   const int32_t* flag = nullptr;
   int want = 0;
 };
 __device__ __forceinline__ bool gated_out(const int32_t* flag, int want) {
-  return flag && __builtin_amdgcn_readfirstlane(*flag) != want;
+  return flag && auto_choice(flag) != want;
 }
 
 // ----------------------------------------------------------------- host launchers
@@ -171,21 +185,35 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
                               int32_t* idx, float* score, float* gate, hipStream_t s);
 size_t router_topk_lds_bytes(int Nr, int Nc, int K);
 
-constexpr int GROUP_HIST_MAX = 16384;  // groups the scatter counts in LDS (32 KB)
 struct SchedPlan {
-  int M, G, rounds, ntiles, passes, digit_bits;  // a tile is rounds x 1024 elements
-  bool group_hist;  // G <= GROUP_HIST_MAX, M <= 8M: the scatter passes also produce group_off
+  int M, G, rounds, ntiles, passes, digit_bits;  // a tile is rounds x 256 elements
   size_t ws_bytes;
   // workspace carve (byte offsets)
-  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals, off_gcount,
-      off_ticket;
+  size_t off_keys_a, off_vals_a, off_keys_b, off_vals_b, off_hist, off_totals;
 };
 SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 // The sorted group ids left in the workspace by the last launch_schedule.
 const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s,
-                           RunGate run = {});
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
+// One stable sort of the elements p < M by idx[p * stride] / B, planned by
+// plan, indices in sorted order to vals_last, buffers in ws.
+struct SortSpec {
+  const int32_t* idx;
+  int stride, M, B;
+  SchedPlan plan;
+  int32_t* vals_last;
+  void* ws;
+};
+// Runs sort a, or with a gate the sort the device's choice selects (b for the
+// blocked form), in one set of launches; both must have the same digit split
+// (plan_schedule with the same N and B).  chosen (optional) receives the
+// choice (0 without a gate).
+hipError_t sort_dual(const SortSpec& a, const SortSpec& b, const int32_t* gate, int32_t* chosen,
+                     hipStream_t s);
+// group_off from the sorted keys a sort with `plan` left in ws
+hipError_t launch_sched_offsets(const SchedPlan& plan, const void* ws, int M, int G,
+                                int32_t* group_off, hipStream_t s, RunGate run = {});
 // order[0..M) = 0..M-1 stably sorted by keys[i] in [0, key_bound); workspace
 // plan_schedule(M, 1, key_bound, 1).ws_bytes
 hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
@@ -193,8 +221,10 @@ hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32
 // order[0..L) = the tokens stably sorted by idx[t*K] / B (the group of each
 // token's first expert); uses the schedule's workspace (plan_schedule(L, K, ..)
 // covers it)
+SortSpec token_order_spec(const int32_t* idx, int L, int K, int64_t N, int B, int32_t* order,
+                          void* ws);
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
-                              int32_t* order, void* ws, hipStream_t s, RunGate gate = {});
+                              int32_t* order, void* ws, hipStream_t s);
 
 // act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order, in
 // chunks along the group boundaries of group_off (B experts per group, G

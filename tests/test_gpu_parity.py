@@ -110,23 +110,21 @@ def test_schedule_on_oracle_routing_is_bit_exact():
 
 
 SCHED_SIZES = [
-    (3000, 100, 50000, 7, None),          # 300,000 tasks: tiles of 2 x 1024, ragged tail
-    (8192, 128, 1700416, 128, None),      # 2^20 tasks: 4 x 1024 per tile
-    (16384, 128, 280900, 64, None),       # 2^21 tasks: 8 x 1024 per tile
-    (16384, 200, 1048576, 128, None),     # 3,276,800 tasks: 16 x 1024 per tile, ragged
+    (3000, 100, 50000, 7, None),          # 300,000 tasks, 2 x 256 per tile, ragged tail
+    (8192, 128, 1700416, 128, None),      # 2^20 tasks: 4 x 256 per tile
+    (16384, 128, 280900, 64, None),       # 2^21 tasks: 8 x 256 per tile
+    (16384, 200, 1048576, 128, None),     # 3,276,800 tasks: 16 x 256 per tile, ragged
     (16384, 128, 1700416, 128, 3000),     # 2^21 tasks on 3000 experts: few, crowded groups
-    (4096, 64, 1700416, 16, None),        # 106,276 groups: three passes, offsets from the keys
-    (16384, 520, 1048576, 128, None),     # 8,519,680 tasks: 64 x 1024 per tile, offsets
-                                          # from the sorted keys
+    (4096, 64, 1700416, 16, None),        # 106,276 groups: three radix passes
+    (16384, 520, 1048576, 128, None),     # 8,519,680 tasks: 2080 tiles of 16 x 256
 ]
 
 
 @pytest.mark.parametrize("case", SCHED_SIZES, ids=lambda c: "L{}_K{}_N{}_B{}_ids{}".format(*c))
 def test_schedule_tile_sizes_are_bit_exact(case):
-    """The radix passes size their tiles by the task count (1 to 64 rounds of
-    1024 tasks), and take the group offsets from the scatter's group counts or,
-    past 16384 groups or 32768 tasks a tile, from the sorted keys; perm and
-    group_off must match the oracle bit for bit at each."""
+    """The radix passes size their tiles by the task count (2 to 16 rounds of
+    256 tasks, past 1024 tiles at the most); perm and group_off must match the
+    oracle bit for bit at each, with one to three radix passes."""
     L, K, N, B, span = case
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     idx_np = rng.integers(0, span or N, size=(L, K), dtype=np.int64)
