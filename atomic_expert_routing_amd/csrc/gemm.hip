@@ -29,8 +29,8 @@ constexpr int GEMM_PLAIN = 0, GEMM_SWIGLU = 1;
 // writes bf16 SiLU(gate) * up to Cb [M, ldc = d_ff].
 //
 // Tiles are (16 MI WVM) x (16 NJ WVN): WVM x WVN waves, each 16 MI x 16 NJ
-// outputs held as MI x NJ MFMA 16x16 accumulators (the default: 128 x 192,
-// 2 x 2 waves of 64 x 96).  The grid is one-dimensional and the tile
+// outputs held as MI x NJ MFMA 16x16 accumulators (three shapes, chosen
+// per product; see below).  The grid is one-dimensional and the tile
 // order is XCD-aware: workgroup b runs on XCD b % 8 and takes tile
 // (b % 8) * per_xcd + b / 8 of the row-major tile order, so that each XCD
 // sweeps a contiguous band of output rows and the x and W panels its
@@ -61,10 +61,10 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
   constexpr int STAGE = TILEA + TILEB;
   constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;           // rows per 1 KB load instruction
-  constexpr int LPWA = TILEA / 1024 / NW; // loads per wave per k-tile, A
-  constexpr int LPWB = TILEB / 1024 / NW; // and B
-  static_assert(TILEA % (1024 * NW) == 0 && TILEB % (1024 * NW) == 0,
-                "tiles must split into 1 KB loads over the waves");
+  constexpr int NLA = TILEA / 1024;       // 1 KB loads per k-tile, A
+  constexpr int NL = NLA + TILEB / 1024;  // and with B
+  constexpr int LPW = (NL + NW - 1) / NW; // loads per wave per k-tile
+  static_assert(TILEA % 1024 == 0 && TILEB % 1024 == 0, "tiles must split into 1 KB loads");
   static_assert(MODE != GEMM_SWIGLU || NJ % 2 == 0, "SwiGLU pairs MFMA column tiles");
   static_assert(S >= 2 && S <= 5, "pipeline depth");
   const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -75,39 +75,41 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave / WVN) * (16 * MI), wn = (wave % WVN) * (16 * NJ);
 
-  // load j of wave w fills bytes [(LPW*w + j) * 1024, +1024) of a tile
-  const uint16_t* asrc[LPWA];
-  const uint16_t* bsrc[LPWB];
+  // The k-tile's A and B bytes form one list of NL 1 KB loads; wave w issues
+  // loads w*LPW .. w*LPW+LPW-1.  When NL is not a multiple of the wave count
+  // the surplus slots repeat the last load (the same bytes to the same LDS
+  // address), so that every wave issues exactly LPW loads and its waits
+  // count exactly.
+  const uint16_t* src[LPW];
+  int dst[LPW];
 #pragma unroll
-  for (int j = 0; j < LPWA; ++j) {
-    const int r = (wave * LPWA + j) * RPI + lane / CPR;
+  for (int j = 0; j < LPW; ++j) {
+    const int l = min(wave * LPW + j, NL - 1);
+    const bool is_a = l < NLA;
+    const int lb = is_a ? l : l - NLA;
+    const int r = lb * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    asrc[j] = A + (size_t)min(tile_m + r, M - 1) * Kd + chunk * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < LPWB; ++j) {
-    const int r = (wave * LPWB + j) * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ chunk_swz<BK>(r);
-    const int gn = min(tile_n + r, N - 1);
-    if constexpr (MODE == GEMM_SWIGLU) {
-      // fused row gn: 16-row blocks alternate gate (B0) and up (B1) rows
-      const int row = (gn >> 5) * 16 + (gn & 15);
-      bsrc[j] = (((gn >> 4) & 1) ? B1 : B0) + (size_t)row * Kd + chunk * 8;
+    dst[j] = (is_a ? 0 : TILEA) + lb * 1024;
+    if (is_a) {
+      src[j] = A + (size_t)min(tile_m + r, M - 1) * Kd + chunk * 8;
     } else {
-      bsrc[j] = (gn < n_split ? B0 + (size_t)gn * Kd : B1 + (size_t)(gn - n_split) * Kd) + chunk * 8;
+      const int gn = min(tile_n + r, N - 1);
+      if constexpr (MODE == GEMM_SWIGLU) {
+        // fused row gn: 16-row blocks alternate gate (B0) and up (B1) rows
+        const int row = (gn >> 5) * 16 + (gn & 15);
+        src[j] = (((gn >> 4) & 1) ? B1 : B0) + (size_t)row * Kd + chunk * 8;
+      } else {
+        src[j] = (gn < n_split ? B0 + (size_t)gn * Kd : B1 + (size_t)(gn - n_split) * Kd) +
+                 chunk * 8;
+      }
     }
   }
   auto issue = [&](int kt) {
     unsigned char* st = gsm + (kt % S) * STAGE;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < LPWA; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[j] + k0),
-                                       (lds_void*)(st + (wave * LPWA + j) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < LPWB; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + k0),
-                                       (lds_void*)(st + TILEA + (wave * LPWB + j) * 1024), 16,
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + k0), (lds_void*)(st + dst[j]), 16,
                                        0, 0);
   };
 
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt landed for this wave; after the barrier it has for every wave,
     // and every wave has finished reading tile kt-1, whose stage is refilled
-    wait_vm_tiles<LPWA + LPWB, S - 2>(min(S - 2, nk - 1 - kt));
+    wait_vm_tiles<LPW, S - 2>(min(S - 2, nk - 1 - kt));
     block_sync_lds();
     if (kt + S - 1 < nk) issue(kt + S - 1);
     const unsigned char* st = gsm + (kt % S) * STAGE;
@@ -192,36 +194,35 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_bt_bf16_pipe(const uint16
     }
 }
 
-// Three tile shapes, chosen per product by its tile count (measured on the
-// products this library runs; TFLOP/s on 2.5 PFLOP/s peak):
-//   huge:  256 x 256, 8 waves (4 x 2) of 64 x 128, BK = 64, 2 stages, 128 KB
-//          of LDS (one workgroup per CU).  Best when the product has at
-//          least two full rounds (512) of such tiles: 16384 x 2608 x 2048
-//          195 us (897; 224 us with the big tile), 4096 x 11008 x 2048 188 us
-//          (980; 202), 4096 x 65536 x 2048 1154 us (953; 1250).  On 4096 x
-//          2608 x 2048 (176 tiles) it takes 71 us against 58.
-//   big:   256 x 192, 8 waves (4 x 2) of 64 x 96, BK = 64, 2 stages, 112 KB
-//          of LDS (one workgroup per CU).  Best when the product has at
-//          least ~200 such tiles: 4096 x 2608 x 2048 56 us (776 TFLOP/s),
-//          4096 x 11008 x 2048 201 us (919).
-//   small: 128 x 128, 4 waves of 64 x 64, BK = 64, 2 stages, 64 KB (two or
-//          three workgroups per CU).  Best below that: 4096 x 2048 x 5504
-//          95 us (976), 2608 x 2048 x 4096 61 us (713).
-// Also measured and dropped: 128 x 192 (4 waves; 59 / 257 / 117 / 67 us on
-// the four products), 256 x 192 with 4 waves of 128 x 96 (BK 32 or 64, 2 or 3
-// stages: one wave per SIMD, 73-284 us), 256 x 256 with 8 waves and BK = 32,
-// 128 x 256.  hipBLASLt (torch.matmul, bf16 out) takes 56 / 186 / 163 / 780 /
-// 84 us on 4096 x 2608 x 2048, 16384 x 2608 x 2048, 4096 x 11008 x 2048,
-// 4096 x 65536 x 2048 and 4096 x 2048 x 5504.  Before the XCD-aware order
-// the 128 x 128 tile took 64 us on the router product (60 us after).
+// Three tile shapes, chosen per product by its tile count.  More waves per
+// CU hide the operand loads better than deeper LDS rings: every shape below
+// beat its 4- or 8-wave form, and 3 to 5 stages of 32-deep k-tiles lost to
+// 2 stages of 64-deep ones (by 5-20%).  Measured, us (TFLOP/s on the
+// 2.5 PFLOP/s bf16 peak), previous shape in brackets:
+//   huge:  256 x 256, 16 waves (8 x 2) of 32 x 128, 128 KB of LDS.  From two
+//          full rounds (512 tiles): 4096 x 11008 x 2048 170 (1088) [200, 8
+//          waves], 4096 x 65536 x 2048 1096 (1003) [1132], 16384 x 2608 x
+//          2048 174 (1007) [179].
+//   big:   256 x 192, 12 waves (4 x 3) of 64 x 64, 112 KB.  From ~200 tiles:
+//          the router product 4096 x 2608 x 2048 49 (893) [59, 8 waves of
+//          64 x 96]; 16 waves of 32 x 96 or 64 x 48 took 50-53.
+//   small: 128 x 128, 8 waves (4 x 2) of 32 x 64, 64 KB (two workgroups per
+//          CU).  Below that: 4096 x 2048 x 1024 25.5 [27.4, 4 waves],
+//          4096 x 1060 x 768 19.4 [22.2], 4096 x 2048 x 5504 88 [90],
+//          2608 x 2048 x 4096 59 [62].
+// Also measured and dropped: 128 x 336 (12 or 14 waves; 49.6-50.9 on the
+// router product, slower elsewhere), 128 x 192 and 128 x 256 with 8 waves,
+// 256 x 176, 256 x 128.  hipBLASLt (torch.matmul, bf16 out) takes 56 / 186 /
+// 163 / 780 / 84 us on 4096 x 2608 x 2048, 16384 x 2608 x 2048, 4096 x
+// 11008 x 2048, 4096 x 65536 x 2048 and 4096 x 2048 x 5504.
 struct GemmCfgHuge {
-  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 8, MI = 4, WVM = 4, WVN = 2;
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 8, MI = 2, WVM = 8, WVN = 2;
 };
 struct GemmCfgBig {
-  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 6, MI = 4, WVM = 4, WVN = 2;
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 4, MI = 4, WVM = 4, WVN = 3;
 };
 struct GemmCfgSmall {
-  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 4, MI = 4, WVM = 2, WVN = 2;
+  static constexpr int BK = GEMM_KTILE, S = 2, NJ = 4, MI = 2, WVM = 4, WVN = 2;
 };
 using GemmCfg = GemmCfgBig;
 constexpr int GEMM_BIG_MIN_TILES = 200;

@@ -564,13 +564,15 @@ def main():
         order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True, tasks=False)[2]
         roofline = blocked_roofline(br, w, expert_mean_ms, order)
         roofline["kernel"] = ("omni_expert_forward_auto, blocked form chosen (auto_clear, "
-                              "auto_mark, auto_choose, token order sort, blk_union, blk_plan, "
-                              "blk_act, blk_out)" if args.assembly == "auto" else roofline["kernel"])
+                              "auto_mark, the token order sort, blk_union, blk_plan, blk_act, "
+                              "blk_out; the per-task launches return at once)"
+                              if args.assembly == "auto" else roofline["kernel"])
     else:
         roofline = {
             "kernel": ("omni_expert_forward_auto, schedule and per-task passes chosen "
-                       "(auto_clear, auto_mark, auto_choose, the schedule's radix sort and "
-                       "sched_offsets, act_plan, expert_act, expert_out_w)"
+                       "(auto_clear, auto_mark, the schedule's radix sort and sched_offsets, "
+                       "act_plan, expert_act, expert_out_w; the blocked launches return at "
+                       "once)"
                        if args.assembly == "auto"
                        else "omni_expert_forward (act_plan, expert_act, expert_out_w)"),
             "bound": "hbm",
