@@ -184,6 +184,13 @@ __device__ __forceinline__ float key_val(unsigned long long k) { return ord_floa
 __device__ __forceinline__ unsigned int key_idx(unsigned long long k) { return ~(unsigned int)k; }
 
 typedef unsigned long long u64;
+// LDS pointers of the top-K: typed in the LDS address space, so that every
+// access is a DS instruction on an LDS offset whatever the compiler inlines
+// (through a generic pointer it may fold a constant part of an index into
+// the instruction offset and leave a base below the LDS window, which the
+// hardware faults on).
+typedef __attribute__((address_space(3))) u64 lds_u64;
+typedef __attribute__((address_space(3))) int lds_int;
 
 // Number of rank pairs (a, b), a < Kr, b < Kc, with (a+1)(b+1) <= K.
 inline int pair_count(int K, int Kr, int Kc) {
@@ -205,7 +212,7 @@ inline int pair_count(int K, int Kr, int Kc) {
 // suffix count sum_{d' >= d} hist[d'] reaches `need`, with that bucket's
 // size (*hd) and the count strictly above it (*above).  Lane l reads bins
 // 4l .. 4l+3.
-__device__ __forceinline__ int find_digit(const int* hist, int need, int* hd, int* above) {
+__device__ __forceinline__ int find_digit(const lds_int* hist, int need, int* hd, int* above) {
   const int lane = threadIdx.x & 63;
   const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
   const int h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
@@ -227,7 +234,7 @@ __device__ __forceinline__ int find_digit(const int* hist, int need, int* hd, in
   return best;
 }
 
-__device__ __forceinline__ void zero_hist(int* hist) {
+__device__ __forceinline__ void zero_hist(lds_int* hist) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
@@ -235,7 +242,7 @@ __device__ __forceinline__ void zero_hist(int* hist) {
 
 // Select the R largest of n unique 64-bit keys in LDS; the R keys are
 // written to out[0..R) in input order.
-__device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* out) {
+__device__ void select_top_lds(const lds_u64* keys, int n, int R, lds_int* hist, lds_u64* out) {
   const int lane = threadIdx.x & 63;
   const u64 lt = (1ull << lane) - 1ull;
   u64 prefix = 0, pmask = 0;
@@ -260,7 +267,9 @@ __device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* ou
       wave_sync();
       for (int i = lane; i < n; i += 64) {
         const u64 k = keys[i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255)], 1);
+        if ((k & pmask) == prefix)
+          __hip_atomic_fetch_add(&hist[(int)((k >> shift) & 255)], 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       wave_sync();
       int hd, above;
@@ -295,7 +304,7 @@ __device__ void select_top_lds(const u64* keys, int n, int R, int* hist, u64* ou
 // subset).  Values equal to T are taken by smallest index.  The R keys are
 // written to out[0..R) in index order.
 template <int VPL>
-__device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, u64* out) {
+__device__ void select_top_regs(const unsigned (&val)[VPL], int n, int R, lds_u64* out) {
   const int lane = threadIdx.x & 63;
   const u64 lt = (1ull << lane) - 1ull;
   auto count_ge = [&](unsigned thr) {  // thr > 0, so padding never counts
@@ -368,7 +377,7 @@ __device__ __forceinline__ u64 wave_umin64(u64 v) {
 // `out` stays a known LDS pointer (DS instructions, no generic addressing).
 template <int Q>
 __device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[Q], int n, int R,
-                                                               u64* out) {
+                                                               lds_u64* out) {
   const int lane = threadIdx.x & 63;
   const u64 lt = (1ull << lane) - 1ull;
   u64 T = 1;  // R >= n: every key is taken
@@ -416,9 +425,11 @@ __device__ __attribute__((always_inline)) void select_top_keys(const u64 (&key)[
 // may fold a constant part of an index into the instruction offset and
 // leave a base below the LDS window, which the hardware faults on.
 template <int Q>
-__device__ __attribute__((always_inline)) void select_cands_regs(const u64* rs, const u64* cs,
-                                                                 const int* off, int Kr, int P,
-                                                                 int Kc, int Nc, int K, u64* fs) {
+__device__ __attribute__((always_inline)) void select_cands_regs(const lds_u64* rs,
+                                                                 const lds_u64* cs,
+                                                                 const lds_int* off, int Kr,
+                                                                 int P, int Kc, int Nc, int K,
+                                                                 lds_u64* fs) {
   const int lane = threadIdx.x & 63;
   const int c0 = lane * Q;
   int a = 0;
@@ -512,7 +523,7 @@ __device__ void wave_sort_desc(u64 (&k)[V]) {
 
 // Sort arr[0..n) (n <= 512) in place, descending.
 template <int V>
-__device__ void wave_sort_lds_t(u64* arr, int n) {
+__device__ void wave_sort_lds_t(lds_u64* arr, int n) {
   const int lane = threadIdx.x & 63;
   u64 k[V];
 #pragma unroll
@@ -523,7 +534,7 @@ __device__ void wave_sort_lds_t(u64* arr, int n) {
     if (v * 64 + lane < n) arr[v * 64 + lane] = k[v];
 }
 
-__device__ void wave_sort_lds(u64* arr, int n) {
+__device__ void wave_sort_lds(lds_u64* arr, int n) {
   if (n <= 64) wave_sort_lds_t<1>(arr, n);
   else if (n <= 128) wave_sort_lds_t<2>(arr, n);
   else if (n <= 256) wave_sort_lds_t<4>(arr, n);
@@ -532,7 +543,7 @@ __device__ void wave_sort_lds(u64* arr, int n) {
 
 // Order the K selected candidates, softmax gate, write the token's outputs.
 template <int V>
-__device__ void emit_topk(const u64* fs, int K, int32_t* idx, float* score, float* gate) {
+__device__ void emit_topk(const lds_u64* fs, int K, int32_t* idx, float* score, float* gate) {
   const int lane = threadIdx.x & 63;
   u64 k[V];
 #pragma unroll
@@ -630,12 +641,12 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_all[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   unsigned char* smem = smem_all + (size_t)wv * lay.bytes;
-  u64* rs = (u64*)(smem + lay.o_rs);
-  u64* cs = (u64*)(smem + lay.o_cs);
-  u64* cand = (u64*)(smem + lay.o_cand);
-  u64* fs = (u64*)(smem + lay.o_fs);
-  int* hist = (int*)(smem + lay.o_hist);
-  int* off = (int*)(smem + lay.o_off);
+  lds_u64* rs = (lds_u64*)(smem + lay.o_rs);
+  lds_u64* cs = (lds_u64*)(smem + lay.o_cs);
+  lds_u64* cand = (lds_u64*)(smem + lay.o_cand);
+  lds_u64* fs = (lds_u64*)(smem + lay.o_fs);
+  lds_int* hist = (lds_int*)(smem + lay.o_hist);
+  lds_int* off = (lds_int*)(smem + lay.o_off);
   const int t = blockIdx.x * wpg + wv, lane = threadIdx.x & 63;
   if (t >= L) return;  // whole wave leaves; no workgroup barrier follows
   const float* sr = logits + (size_t)t * (Nr + Nc);

@@ -131,12 +131,16 @@ def test_backward_is_deterministic():
         assert torch.equal(a[k][:n], b[k][:n]), k
 
 
-@pytest.mark.parametrize("name", [synth.HEADLINE])
+@pytest.mark.parametrize("name", [synth.HEADLINE, "skewed_L16384_N1700416_d2048"])
 def test_full_size_backward_sampled(name):
-    """The 4096-token, 1.7M-expert shape: used-expert list in full, dx and
-    dgate on sampled tokens, dW and dV on sampled experts, dW_r and dW_c in
-    full (the oracle's dense products over all tokens)."""
+    """The 4096-token, 1.7M-expert shape and the skewed 16384-token one (K =
+    256, tasks piled onto few experts): used-expert list in full, dx and
+    dgate on sampled tokens, dW and dV on sampled experts (every task of
+    each; fewer experts on the skewed routing, whose experts carry hundreds
+    of tasks), dW_r and dW_c in full (the oracle's dense products over all
+    tokens)."""
     w = synth.WORKLOADS[name]
+    n_exp = 16 if w.x_dist == "normal" else 6
     say(f"full-size backward {name}: inputs and forward routing")
     inp = synth.make_inputs(w, seed=0, device="cuda")
     br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
@@ -161,9 +165,10 @@ def test_full_size_backward_sampled(name):
     dx_o = BO.input_grad_expert(Wd, sub_idx, terms["dh"])
     check_y(to_np(g["dx"])[toks], dx_o, RTOL_FP32_ARITH)
     # sampled experts (first, last and spread): every task of each
-    pick = np.unique(np.concatenate([[0, g["n"] - 1], rs.choice(g["n"], 16, replace=False)]))
+    pick = np.unique(np.concatenate([[0, g["n"] - 1], rs.choice(g["n"], n_exp, replace=False)]))
     ex = uniq_o[pick]
     m_all = np.nonzero(np.isin(idx.reshape(-1), ex))[0]
+    say(f"  {len(ex)} sampled experts, {m_all.size} tasks")
     t_all = np.unique(m_all // w.K)
     x_rows = to_np(inp["x"][torch.as_tensor(t_all, device="cuda")]).astype(np.float64)
     dy_rows = to_np(dy[torch.as_tensor(t_all, device="cuda")]).astype(np.float64)

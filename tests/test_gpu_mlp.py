@@ -33,8 +33,8 @@ def need_gpu():
 def check_mlp(x, Wg, Wu, Wd, got, base=None):
     """got = base + MLP(x) on the rows given; returns the worst bound ratio."""
     x, Wg, Wu, Wd = (to_np(t).astype(np.float64) for t in (x, Wg, Wu, Wd))
-    a = O.silu(x @ Wg.T) * (x @ Wu.T)
-    want = a @ Wd.T
+    want = O.shared_mlp(x, Wg, Wu, Wd)
+    a = O.silu(x @ Wg.T) * (x @ Wu.T)  # the intermediate, for the size of the bound
     got = to_np(got).astype(np.float64)
     if base is not None:
         got = got - to_np(base).astype(np.float64)
