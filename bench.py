@@ -84,25 +84,38 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-ASSEMBLY_SRC = os.path.join(ROOT, "atomic_expert_routing_amd", "csrc", "assembly.hip")
-PROFILE = os.path.join(ROOT, "profiles", "routed_forward_L4096_N1700416_d2048.md")
+CSRC = os.path.join(ROOT, "atomic_expert_routing_amd", "csrc")
+# the sources of every kernel an automatic-assembly call launches
+TRAFFIC_SRCS = ("assembly.hip", "schedule.hip", "blocked.hip", "omni_internal.h")
+
+
+def profile_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"routed_forward_{workload_name}.md")
+
+
+def sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in TRAFFIC_SRCS:
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_name, assembly):
     """Counter-measured bytes per assembly call from the committed rocprofv3
-    summary, or None when it was taken on other kernel source, another
-    workload or another assembly."""
-    import hashlib
+    summary of this workload, or None when there is none for this assembly
+    or it was taken on other kernel source."""
     import re
 
-    if workload_name != "L4096_N1700416_d2048" or not os.path.exists(PROFILE):
+    path = profile_path(workload_name)
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE).read()
-    m_hash = re.search(r"assembly\.hip sha256: ([0-9a-f]{64})", text)
+    text = open(path).read()
+    m_hash = re.search(r"kernel sources sha256 \([^)]*\): ([0-9a-f]{64})", text)
     m_bytes = re.search(r"assembly call traffic bytes \(%s\): (\d+)" % assembly, text)
-    if not (m_hash and m_bytes):
-        return None
-    if hashlib.sha256(open(ASSEMBLY_SRC, "rb").read()).hexdigest() != m_hash.group(1):
+    if not (m_hash and m_bytes) or m_hash.group(1) != sources_sha256():
         return None
     return int(m_bytes.group(1))
 
@@ -563,6 +576,7 @@ def main():
     if chosen:
         order = omni.omni_schedule(br.idx, w.N, w.B, token_order=True, tasks=False)[2]
         roofline = blocked_roofline(br, w, expert_mean_ms, order)
+        roofline["traffic"] = measured_traffic(w.name, args.assembly)
         roofline["kernel"] = ("omni_expert_forward_auto, blocked form chosen (auto_clear, "
                               "auto_mark, the token order sort, blk_union, blk_plan, blk_act, "
                               "blk_out; the per-task launches return at once)"
