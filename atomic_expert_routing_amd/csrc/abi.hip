@@ -129,6 +129,13 @@ omni_status expert_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype
   return OMNI_OK;
 }
 
+omni_status auto_bwd_ws(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt, size_t* out) {
+  omni_status s;
+  if ((s = expert_bwd_ws(L, d, N, K, dt, out)) != OMNI_OK) return s;
+  *out = omni::plan_expert_backward_auto(L, d, N, K, dt).ws_bytes;
+  return OMNI_OK;
+}
+
 omni_status router_bwd_ws(int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t K, omni_dtype dt,
                           size_t* out) {
   omni_status s;
@@ -468,6 +475,34 @@ omni_status omni_expert_backward_blocked(const void* x, const void* W, const voi
   return hip_status(e, "blocked expert backward launch");
 }
 
+omni_status omni_expert_backward_auto(const void* x, const void* W, const void* V,
+                                      const int32_t* idx, const float* gate, const float* dy,
+                                      int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt,
+                                      float* dx, float* dgate, int32_t* uniq, int32_t* n_uniq,
+                                      omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                      int32_t* chosen, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  omni_status s = auto_bwd_ws(L, d, N, K, dt, &need);
+  if (s != OMNI_OK) return s;
+  if (!x || !W || !V || !idx || !gate || !dy || !dx || !dgate || !uniq || !n_uniq || !dW_rows ||
+      !dV_rows)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_backward_auto: NULL array pointer");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(dy) || !aligned16(dx) ||
+      !aligned16(dW_rows) || !aligned16(dV_rows))
+    return fail(OMNI_ERR_INVALID_ARG,
+                "omni_expert_backward_auto: x, W, V, dy, dx, dW_rows and dV_rows must be 16-byte "
+                "aligned");
+  if (grad_dt != OMNI_F32 && grad_dt != OMNI_BF16)
+    return fail(OMNI_ERR_INVALID_ARG, "omni_expert_backward_auto: unknown grad_dt %d",
+                (int)grad_dt);
+  if ((s = check_ws(ws, ws_bytes, need)) != OMNI_OK) return s;
+  const omni::AutoBwdPlan plan = omni::plan_expert_backward_auto(L, d, N, K, dt);
+  hipError_t e = omni::launch_expert_backward_auto(
+      x, W, V, idx, gate, dy, (int)L, (int)d, (int)N, (int)K, dt, dx, dgate, uniq, n_uniq,
+      grad_dt, dW_rows, dV_rows, chosen, plan, ws, (hipStream_t)stream);
+  return hip_status(e, "automatic expert backward launch");
+}
+
 omni_status omni_router_backward(const void* x, const void* Wr, const void* Wc,
                                  const int32_t* idx, const float* gate, const float* dgate,
                                  int64_t L, int64_t d, int64_t Nr, int64_t Nc, int64_t K,
@@ -555,6 +590,7 @@ omni_status omni_workspace_bytes(omni_op op, int64_t L, int64_t d, int64_t Nr, i
     case OMNI_OP_EXPERT_FORWARD_BLOCKED: s = blocked_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_EXPERT_BACKWARD_BLOCKED: s = blocked_bwd_ws(L, d, N, K, dt, &need); break;
     case OMNI_OP_EXPERT_FORWARD_AUTO: s = expert_auto_ws(L, d, N, K, B, dt, &need); break;
+    case OMNI_OP_EXPERT_BACKWARD_AUTO: s = auto_bwd_ws(L, d, N, K, dt, &need); break;
     default: return fail(OMNI_ERR_INVALID_ARG, "unknown op %d", (int)op);
   }
   if (s != OMNI_OK) return s;

@@ -551,7 +551,27 @@ __global__ __launch_bounds__(AUTO_MARK_THREADS) void auto_mark(
   }
 }
 
+__global__ void set_i32(int32_t* __restrict__ p, int v) { p[0] = v; }
+
 }  // namespace
+
+int auto_sample_size(int64_t M) { return (int)std::min<int64_t>(M, AUTO_SAMPLE); }
+
+hipError_t launch_auto_sample(const int32_t* idx, int M, int64_t N, uint32_t* bits, int32_t* gate,
+                              hipStream_t s) {
+  const int nwords = (int)((N + 31) / 32);
+  const int S = auto_sample_size(M);
+  hipLaunchKernelGGL(auto_clear, dim3((unsigned)std::min(512, (nwords + 255) / 256)), dim3(256),
+                     0, s, bits, nwords, gate, S);
+  hipLaunchKernelGGL(auto_mark, dim3((unsigned)((S + AUTO_MARK_THREADS - 1) / AUTO_MARK_THREADS)),
+                     dim3(AUTO_MARK_THREADS), 0, s, idx, M, (int)N, S, bits, gate + 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_i32(int32_t* p, int v, hipStream_t s) {
+  hipLaunchKernelGGL(set_i32, dim3(1), dim3(1), 0, s, p, v);
+  return hipGetLastError();
+}
 
 int expert_act_chunks(int64_t M) { return (int)((M + ACT_CHUNK - 1) / ACT_CHUNK); }
 
@@ -617,7 +637,7 @@ AutoPlan plan_expert_auto(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B,
   AutoPlan p{};
   const int64_t M = L * K;
   p.G = (int)((N + B - 1) / B);
-  p.sample = (int)std::min<int64_t>(M, AUTO_SAMPLE);
+  p.sample = auto_sample_size(M);
   p.sched = plan_schedule(L, K, N, B);
   p.blocked_ok = dt == OMNI_BF16 && d % BLK_D_TILE == 0 && L <= INT32_MAX - BLK_TOKENS;
   size_t o = 0;
@@ -660,13 +680,8 @@ hipError_t launch_expert_auto(const void* x, const void* W, const void* V, const
   int32_t* choice = nullptr;  // the run gate: [1] distinct experts, [2] sample size
   if (p.blocked_ok) {
     choice = (int32_t*)(w + p.off_flag);
-    uint32_t* bits = (uint32_t*)(w + p.off_bits);
-    const int nwords = (int)((N + 31) / 32);
-    hipLaunchKernelGGL(auto_clear, dim3((unsigned)std::min(512, (nwords + 255) / 256)),
-                       dim3(256), 0, s, bits, nwords, choice, p.sample);
-    hipLaunchKernelGGL(auto_mark, dim3((unsigned)((p.sample + AUTO_MARK_THREADS - 1) /
-                                                  AUTO_MARK_THREADS)),
-                       dim3(AUTO_MARK_THREADS), 0, s, idx, M, (int)N, p.sample, bits, choice + 1);
+    e = launch_auto_sample(idx, M, N, (uint32_t*)(w + p.off_bits), choice, s);
+    if (e != hipSuccess) return e;
     per_task = RunGate{choice, 0};
     blocked = RunGate{choice, 1};
   }

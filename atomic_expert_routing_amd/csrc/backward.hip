@@ -82,7 +82,9 @@ __global__ __launch_bounds__(256) void expert_bwd_token(
     const uint16_t* __restrict__ x_, const uint16_t* __restrict__ W_, const uint16_t* __restrict__ V_,
     const int32_t* __restrict__ idx, const float* __restrict__ gate, const float* __restrict__ dy,
     const int32_t* __restrict__ n_uniq, int d, int K, float* __restrict__ dx,
-    float* __restrict__ dgate, float* __restrict__ dh_out, float* __restrict__ ga_out) {
+    float* __restrict__ dgate, float* __restrict__ dh_out, float* __restrict__ ga_out,
+    const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   using C = Chunk<BF16>;
   constexpr int E = C::E;
   extern __shared__ __attribute__((aligned(16))) float red[];  // [BWD_WAVES][d]
@@ -287,7 +289,9 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_write(const int32_t* __restri
 __global__ __launch_bounds__(256) void row_keys(const int32_t* __restrict__ perm,
                                                 const int32_t* __restrict__ seg,
                                                 const int32_t* __restrict__ n_uniq, int K, int Lq,
-                                                int U, int32_t* __restrict__ key) {
+                                                int U, int32_t* __restrict__ key,
+                                                const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   const int n = *n_uniq;
   for (int u = blockIdx.x * 256 + threadIdx.x; u < U; u += gridDim.x * 256) {
     int k = 8 * Lq;
@@ -310,7 +314,9 @@ __global__ __launch_bounds__(256) void row_recs(const int32_t* __restrict__ rord
                                                 const int32_t* __restrict__ seg,
                                                 const int32_t* __restrict__ perm,
                                                 const int32_t* __restrict__ n_uniq, int Lq,
-                                                int4* __restrict__ rec) {
+                                                int4* __restrict__ rec, const int32_t* run_flag,
+                                                int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int off[9];
   if (threadIdx.x < 9) off[threadIdx.x] = goff[threadIdx.x * Lq];
   __syncthreads();
@@ -402,7 +408,9 @@ __global__ __launch_bounds__(512) void expert_bwd_rows(
     const uint16_t* __restrict__ x_, const float* __restrict__ dy, const int32_t* __restrict__ perm,
     const int4* __restrict__ rec, const int32_t* __restrict__ n_uniq,
     const float* __restrict__ dh, const float* __restrict__ ga, int d, int K,
-    void* __restrict__ dW_rows, void* __restrict__ dV_rows) {
+    void* __restrict__ dW_rows, void* __restrict__ dV_rows, const int32_t* run_flag,
+    int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   using C = Chunk<BF16>;
   constexpr int E = C::E;
   const int b = blockIdx.x;
@@ -583,14 +591,14 @@ template <bool BF16>
 hipError_t launch_bwd_token_t(const void* x, const void* W, const void* V, const int32_t* idx,
                               const float* gate, const float* dy, const int32_t* n_uniq, int L,
                               int d, int K, float* dx, float* dgate, float* dh, float* ga,
-                              hipStream_t s) {
+                              hipStream_t s, RunGate run) {
   const int nch = (int)(((size_t)d * (BF16 ? 2 : 4) / 16 + 63) / 64);
   const size_t lds = (size_t)BWD_WAVES * d * 4;
   const uint16_t *xp = (const uint16_t*)x, *wp = (const uint16_t*)W, *vp = (const uint16_t*)V;
 #define OMNI_BT(N)                                                                            \
   case N:                                                                                     \
     hipLaunchKernelGGL((expert_bwd_token<BF16, N>), dim3(L), dim3(256), lds, s, xp, wp, vp, idx, \
-                       gate, dy, n_uniq, d, K, dx, dgate, dh, ga);                            \
+                       gate, dy, n_uniq, d, K, dx, dgate, dh, ga, run.flag, run.want);        \
     break;
   switch (nch) {
     OMNI_BT(1) OMNI_BT(2) OMNI_BT(3) OMNI_BT(4) OMNI_BT(5) OMNI_BT(6) OMNI_BT(7) OMNI_BT(8)
@@ -642,17 +650,27 @@ hipError_t launch_expert_backward(const void* x, const void* W, const void* V, c
                                   omni_dtype dt, float* dx, float* dgate, int32_t* uniq,
                                   int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s) {
-  char* w = (char*)ws;
-  float* dh = (float*)(w + p.off_dh);
-  float* ga = (float*)(w + p.off_ga);
-  const bool bf = dt == OMNI_BF16;
   // the sort by expert first: the per-token pass reads the used-expert count
   hipError_t e = launch_expert_segments(idx, N, uniq, n_uniq, p, ws, s);
   if (e != hipSuccess) return e;
-  e = bf ? launch_bwd_token_t<true>(x, W, V, idx, gate, dy, n_uniq, L, d, K, dx, dgate, dh, ga, s)
-         : launch_bwd_token_t<false>(x, W, V, idx, gate, dy, n_uniq, L, d, K, dx, dgate, dh, ga, s);
+  e = launch_expert_bwd_token(x, W, V, idx, gate, dy, L, d, K, dt, dx, dgate, n_uniq, p, ws, s);
   if (e != hipSuccess) return e;
   return launch_expert_grad_rows(x, dy, d, K, dt, n_uniq, grad_dt, dW_rows, dV_rows, p, ws, s);
+}
+
+hipError_t launch_expert_bwd_token(const void* x, const void* W, const void* V,
+                                   const int32_t* idx, const float* gate, const float* dy, int L,
+                                   int d, int K, omni_dtype dt, float* dx, float* dgate,
+                                   const int32_t* n_uniq, const BwdPlan& p, void* ws,
+                                   hipStream_t s, RunGate run) {
+  char* w = (char*)ws;
+  float* dh = (float*)(w + p.off_dh);
+  float* ga = (float*)(w + p.off_ga);
+  return dt == OMNI_BF16
+             ? launch_bwd_token_t<true>(x, W, V, idx, gate, dy, n_uniq, L, d, K, dx, dgate, dh, ga,
+                                        s, run)
+             : launch_bwd_token_t<false>(x, W, V, idx, gate, dy, n_uniq, L, d, K, dx, dgate, dh, ga,
+                                         s, run);
 }
 
 hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int32_t* n_uniq,
@@ -675,7 +693,8 @@ hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int3
 
 hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K, omni_dtype dt,
                                    const int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
-                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s) {
+                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s,
+                                   RunGate run) {
   char* w = (char*)ws;
   float* dh = (float*)(w + p.off_dh);
   float* ga = (float*)(w + p.off_ga);
@@ -687,12 +706,12 @@ hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K,
   int4* rec = (int4*)(w + p.off_rec);
   const unsigned ogrid = (unsigned)std::min(2048, (p.U_max + 255) / 256);
   hipLaunchKernelGGL(row_keys, dim3(ogrid), dim3(256), 0, s, perm, seg, n_uniq, K, p.Lq, p.U_max,
-                     rkey);
+                     rkey, run.flag, run.want);
   hipError_t e = launch_schedule(rkey, p.U_max, 1, 8 * p.Lq + 1, p.rsort, rord, goff,
-                                 w + p.off_sched, s);
+                                 w + p.off_sched, s, run);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_recs, dim3(ogrid), dim3(256), 0, s, rord, goff, seg, perm, n_uniq, p.Lq,
-                     rec);
+                     rec, run.flag, run.want);
   const bool bf = dt == OMNI_BF16;
   const int E = bf ? 8 : 4;
   const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
@@ -700,7 +719,7 @@ hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K,
   const bool obf = grad_dt == OMNI_BF16;
 #define OMNI_ROWS(IB, OB)                                                                        \
   hipLaunchKernelGGL((expert_bwd_rows<IB, OB>), grid, dim3(threads), 0, s, (const uint16_t*)x, dy, \
-                     perm, rec, n_uniq, dh, ga, d, K, dW_rows, dV_rows)
+                     perm, rec, n_uniq, dh, ga, d, K, dW_rows, dV_rows, run.flag, run.want)
   if (bf && obf) OMNI_ROWS(true, true);
   else if (bf) OMNI_ROWS(true, false);
   else if (obf) OMNI_ROWS(false, true);

@@ -724,7 +724,9 @@ __global__ __launch_bounds__(256) void blk_out(const uint16_t* __restrict__ V,
 
 // pos[order[s]] = s
 __global__ __launch_bounds__(256) void inv_order(const int32_t* __restrict__ order, int L,
-                                                 int32_t* __restrict__ pos) {
+                                                 int32_t* __restrict__ pos,
+                                                 const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   for (int s = blockIdx.x * 256 + threadIdx.x; s < L; s += gridDim.x * 256) {
     const int t = order[s];
     if ((unsigned)t < (unsigned)L) pos[t] = s;
@@ -737,7 +739,9 @@ __global__ __launch_bounds__(256) void set_keys(const int32_t* __restrict__ perm
                                                 const int32_t* __restrict__ seg,
                                                 const int32_t* __restrict__ n_uniq,
                                                 const int32_t* __restrict__ pos, int K, int L,
-                                                int ucap_e, int32_t* __restrict__ key) {
+                                                int ucap_e, int32_t* __restrict__ key,
+                                                const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   const int n = *n_uniq, lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;
   for (int u = blockIdx.x * 4 + (threadIdx.x >> 6); u < ucap_e; u += nw) {
@@ -761,7 +765,9 @@ __global__ __launch_bounds__(1024) void set_union(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ seg, int K, int L,
     const int32_t* __restrict__ stoff, const float* __restrict__ dh, const float* __restrict__ ga,
     int32_t* __restrict__ nS, int32_t* __restrict__ T, uint16_t* __restrict__ dht_hi,
-    uint16_t* __restrict__ dht_lo, uint16_t* __restrict__ gat_hi, uint16_t* __restrict__ gat_lo) {
+    uint16_t* __restrict__ dht_lo, uint16_t* __restrict__ gat_hi, uint16_t* __restrict__ gat_lo,
+    const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   extern __shared__ unsigned bm[];  // W bitmap words, then their prefix
   __shared__ int wtot[16];
   const int W = (L + 31) / 32;
@@ -844,7 +850,9 @@ __global__ __launch_bounds__(1024) void set_union(
 // sets (the capacity slots past them have none); stoff[smax] = all tiles
 __global__ __launch_bounds__(1024) void set_plan(const int32_t* __restrict__ nS,
                                                  const int32_t* __restrict__ n_uniq, int smax,
-                                                 int32_t* __restrict__ stoff) {
+                                                 int32_t* __restrict__ stoff,
+                                                 const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   __shared__ int wtot[16];
   const int tid = threadIdx.x;
   const int nsets = (*n_uniq + BT - 1) / BT;
@@ -930,7 +938,9 @@ int act_grid(const BlockedPlan& p) {
 // dy = dy_hi + dy_lo, two bf16 terms (round to nearest even, then the rest)
 __global__ __launch_bounds__(256) void split_bf16(const float* __restrict__ a, size_t n,
                                                   uint16_t* __restrict__ hi,
-                                                  uint16_t* __restrict__ lo) {
+                                                  uint16_t* __restrict__ lo,
+                                                  const int32_t* run_flag, int run_want) {
+  if (gated_out(run_flag, run_want)) return;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const float v = a[i];
     const uint16_t h = bf16_rne(v);
@@ -999,7 +1009,8 @@ hipError_t launch_expert_backward_blocked(const void* x, const void* W, const vo
                                           const int32_t* order, int L, int d, int N, int K,
                                           float* dx, float* dgate, int32_t* uniq, int32_t* n_uniq,
                                           omni_dtype grad_dt, void* dW_rows, void* dV_rows,
-                                          const BlockedBwdPlan& p, void* ws, hipStream_t s) {
+                                          const BlockedBwdPlan& p, void* ws, hipStream_t s,
+                                          RunGate run, bool segments_done) {
   char* w = (char*)ws;
   char* wb = w + p.off_blk;
   const BlockedPlan& bp = p.blk;
@@ -1028,48 +1039,123 @@ hipError_t launch_expert_backward_blocked(const void* x, const void* W, const vo
   uint16_t* gat_hi = (uint16_t*)(w + p.off_gat);
   uint16_t* gat_lo = (uint16_t*)(w + p.off_gat + term);
   // 1. per token block: dgate, the per-task terms dh and g SiLU(h), and dx
-  hipError_t e = launch_union_plan(idx, gate, order, L, K, bp, wb, kmap, s);
+  hipError_t e = launch_union_plan(idx, gate, order, L, K, bp, wb, kmap, s, run);
   if (e != hipSuccess) return e;
   const size_t n = (size_t)L * d;
   hipLaunchKernelGGL(split_bf16, dim3((unsigned)std::min<size_t>((n + 255) / 256, 8192)), dim3(256),
-                     0, s, dy, n, dyh, dyl);
+                     0, s, dy, n, dyh, dyl, run.flag, run.want);
   hipLaunchKernelGGL(blk_act<BLK_BWD>, dim3(act_grid(bp)), dim3(256), K1_S * K1_STAGE, s,
                      (const uint16_t*)x, (const uint16_t*)W, dyh, dyl, (const uint16_t*)V, order, U,
-                     toff, G, kmap, L, d, K, bp.nb, bp.ucap, dHhi, dHlo, dgate, dh, ga, nullptr, 0);
+                     toff, G, kmap, L, d, K, bp.nb, bp.ucap, dHhi, dHlo, dgate, dh, ga, run.flag,
+                     run.want);
   // dx = dH W[U], the forward's second product with W in place of V
   hipLaunchKernelGGL((blk_out<false, 1, false>), dim3(bp.nb * (d / K2_COLS)), dim3(256),
                      K2_S * K2_STAGE, s, (const uint16_t*)W, nullptr, order, nullptr, U, toff, dHhi,
-                     dHlo, L, d, bp.ucap, (void*)dx, nullptr, 0);
-  // 2. the used experts, then the expert sets and their dW, dV rows
-  if ((e = launch_expert_segments(idx, N, uniq, n_uniq, p.bwd, wr, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(inv_order, dim3((L + 255) / 256), dim3(256), 0, s, order, L, pos);
+                     dHlo, L, d, bp.ucap, (void*)dx, run.flag, run.want);
+  // 2. the used experts (unless the caller has them already), then the expert
+  // sets and their dW, dV rows
+  if (!segments_done &&
+      (e = launch_expert_segments(idx, N, uniq, n_uniq, p.bwd, wr, s)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(inv_order, dim3((L + 255) / 256), dim3(256), 0, s, order, L, pos, run.flag,
+                     run.want);
   hipLaunchKernelGGL(set_keys, dim3((unsigned)std::min(2048, (p.ucap_e + 3) / 4)), dim3(256), 0, s,
-                     perm, seg, n_uniq, pos, K, L, p.ucap_e, key);
-  if ((e = launch_sort_keys(key, p.ucap_e, (int64_t)L + 1, eord, w + p.off_ksort, s)) != hipSuccess)
+                     perm, seg, n_uniq, pos, K, L, p.ucap_e, key, run.flag, run.want);
+  if ((e = launch_sort_keys(key, p.ucap_e, (int64_t)L + 1, eord, w + p.off_ksort, s, run)) !=
+      hipSuccess)
     return e;
   const size_t lds_s = (size_t)2 * ((L + 31) / 32) * 4;
   const dim3 sgrid((unsigned)std::min(p.smax, MI355X_CUS));
   hipLaunchKernelGGL(set_union<true>, sgrid, dim3(1024), lds_s, s, eord, n_uniq, perm, seg, K, L,
-                     nullptr, nullptr, nullptr, nS, nullptr, nullptr, nullptr, nullptr, nullptr);
-  hipLaunchKernelGGL(set_plan, dim3(1), dim3(1024), 0, s, nS, n_uniq, p.smax, stoff);
+                     nullptr, nullptr, nullptr, nS, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     run.flag, run.want);
+  hipLaunchKernelGGL(set_plan, dim3(1), dim3(1024), 0, s, nS, n_uniq, p.smax, stoff, run.flag,
+                     run.want);
   hipLaunchKernelGGL(set_union<false>, sgrid, dim3(1024), lds_s, s, eord, n_uniq, perm, seg, K, L,
-                     stoff, dh, ga, nullptr, T, dht_hi, dht_lo, gat_hi, gat_lo);
+                     stoff, dh, ga, nullptr, T, dht_hi, dht_lo, gat_hi, gat_lo, run.flag,
+                     run.want);
   const bool obf = grad_dt == OMNI_BF16;
   const dim3 ogrid((unsigned)std::min(p.smax * (d / K2_COLS), 2 * MI355X_CUS));
   const dim3 ogrid2((unsigned)std::min(p.smax * (d / K2_COLS), MI355X_CUS));
   constexpr size_t lds1 = K2_S * (K2_VT + 2 * K2_AT), lds2 = K2_S * (2 * K2_VT + 2 * K2_AT);
   if (obf) {
     hipLaunchKernelGGL((blk_out<true, 1, true>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
-                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, nullptr, 0);
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, run.flag,
+                       run.want);
     hipLaunchKernelGGL((blk_out<true, 2, true>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord, n_uniq,
-                       T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, nullptr, 0);
+                       T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, run.flag, run.want);
   } else {
     hipLaunchKernelGGL((blk_out<true, 1, false>), ogrid, dim3(256), lds1, s, (const uint16_t*)x,
-                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, nullptr, 0);
+                       nullptr, eord, n_uniq, T, stoff, dht_hi, dht_lo, L, d, 0, dW_rows, run.flag,
+                       run.want);
     hipLaunchKernelGGL((blk_out<true, 2, false>), ogrid2, dim3(256), lds2, s, dyh, dyl, eord,
-                       n_uniq, T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, nullptr, 0);
+                       n_uniq, T, stoff, gat_hi, gat_lo, L, d, 0, dV_rows, run.flag, run.want);
   }
   return hipGetLastError();
+}
+
+AutoBwdPlan plan_expert_backward_auto(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt) {
+  auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  AutoBwdPlan p{};
+  p.blocked_ok = dt == OMNI_BF16 && d % BLK_D_TILE == 0 && L <= BLK_BWD_MAX_L;
+  size_t o = 0;
+  if (p.blocked_ok) {
+    p.blk = plan_expert_backward_blocked(L, d, N, K);
+    p.order_sort = plan_schedule(L, 1, N, 1);
+    p.off_flag = o;   o += 256;  // [1] distinct experts in the sample, [2] the sample size
+    p.off_bits = o;   o += a256((size_t)((N + 31) / 32) * 4);
+    p.off_order = o;  o += a256((size_t)L * 4);
+    p.off_osort = o;  o += a256(p.order_sort.ws_bytes);
+    p.off_main = o;   o += a256(p.blk.ws_bytes);
+  } else {
+    p.bwd = plan_expert_backward(L, d, N, K);
+    p.off_flag = p.off_bits = p.off_order = p.off_osort = 0;
+    p.off_main = o;   o += a256(p.bwd.ws_bytes);
+  }
+  p.ws_bytes = o;
+  return p;
+}
+
+hipError_t launch_expert_backward_auto(const void* x, const void* W, const void* V,
+                                       const int32_t* idx, const float* gate, const float* dy,
+                                       int L, int d, int N, int K, omni_dtype dt, float* dx,
+                                       float* dgate, int32_t* uniq, int32_t* n_uniq,
+                                       omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                       int32_t* chosen, const AutoBwdPlan& p, void* ws,
+                                       hipStream_t s) {
+  char* w = (char*)ws;
+  hipError_t e;
+  if (!p.blocked_ok) {  // the blocked form cannot take these inputs
+    if (chosen && (e = launch_set_i32(chosen, 0, s)) != hipSuccess) return e;
+    return launch_expert_backward(x, W, V, idx, gate, dy, L, d, N, K, dt, dx, dgate, uniq, n_uniq,
+                                  grad_dt, dW_rows, dV_rows, p.bwd, w + p.off_main, s);
+  }
+  int32_t* choice = (int32_t*)(w + p.off_flag);
+  if ((e = launch_auto_sample(idx, L * K, N, (uint32_t*)(w + p.off_bits), choice, s)) !=
+      hipSuccess)
+    return e;
+  const RunGate per_task{choice, 0}, blocked{choice, 1};
+  char* wm = w + p.off_main;
+  char* wt = wm + p.blk.off_bwd;  // the per-task plan's region, used by both forms
+  int32_t* order = (int32_t*)(w + p.off_order);
+  // the blocked form's token order (tokens sorted by their first expert);
+  // its first launch records the choice
+  if ((e = launch_token_order(idx, L, K, N, 1, order, w + p.off_osort, s, blocked, chosen)) !=
+      hipSuccess)
+    return e;
+  // both forms: the tasks sorted by expert, the used experts and segments
+  if ((e = launch_expert_segments(idx, N, uniq, n_uniq, p.blk.bwd, wt, s)) != hipSuccess) return e;
+  // per-task form
+  if ((e = launch_expert_bwd_token(x, W, V, idx, gate, dy, L, d, K, dt, dx, dgate, n_uniq,
+                                   p.blk.bwd, wt, s, per_task)) != hipSuccess)
+    return e;
+  if ((e = launch_expert_grad_rows(x, dy, d, K, dt, n_uniq, grad_dt, dW_rows, dV_rows, p.blk.bwd,
+                                   wt, s, per_task)) != hipSuccess)
+    return e;
+  // blocked form
+  return launch_expert_backward_blocked(x, W, V, idx, gate, dy, order, L, d, N, K, dx, dgate, uniq,
+                                        n_uniq, grad_dt, dW_rows, dV_rows, p.blk, wm, s, blocked,
+                                        /*segments_done=*/true);
 }
 
 }  // namespace omni

@@ -194,8 +194,10 @@ struct SchedPlan {
 SchedPlan plan_schedule(int64_t L, int64_t K, int64_t N, int64_t B);
 // The sorted group ids left in the workspace by the last launch_schedule.
 const int32_t* schedule_sorted_keys(const SchedPlan& plan, const void* ws);
+// (with a gate: only when the device's choice equals run.want)
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s);
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s,
+                           RunGate run = {});
 // One stable sort of the elements p < M by idx[p * stride] / B, planned by
 // plan, indices in sorted order to vals_last, buffers in ws.
 struct SortSpec {
@@ -211,20 +213,24 @@ struct SortSpec {
 // choice (0 without a gate).
 hipError_t sort_dual(const SortSpec& a, const SortSpec& b, const int32_t* gate, int32_t* chosen,
                      hipStream_t s);
+// One sort, run only when the device's choice equals run.want (always
+// without a gate); chosen (optional) receives the choice.
+hipError_t sort_gated(const SortSpec& a, RunGate run, int32_t* chosen, hipStream_t s);
 // group_off from the sorted keys a sort with `plan` left in ws
 hipError_t launch_sched_offsets(const SchedPlan& plan, const void* ws, int M, int G,
                                 int32_t* group_off, hipStream_t s, RunGate run = {});
 // order[0..M) = 0..M-1 stably sorted by keys[i] in [0, key_bound); workspace
 // plan_schedule(M, 1, key_bound, 1).ws_bytes
 hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
-                            void* ws, hipStream_t s);
+                            void* ws, hipStream_t s, RunGate run = {});
 // order[0..L) = the tokens stably sorted by idx[t*K] / B (the group of each
 // token's first expert); uses the schedule's workspace (plan_schedule(L, K, ..)
 // covers it)
 SortSpec token_order_spec(const int32_t* idx, int L, int K, int64_t N, int B, int32_t* order,
                           void* ws);
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
-                              int32_t* order, void* ws, hipStream_t s);
+                              int32_t* order, void* ws, hipStream_t s, RunGate run = {},
+                              int32_t* chosen = nullptr);
 
 // act[m] = gate[m] * SiLU(x[m/K] . W[idx[m]]) for m in schedule order, in
 // chunks along the group boundaries of group_off (B experts per group, G
@@ -273,6 +279,13 @@ struct AutoPlan {
   size_t ws_bytes;
 };
 AutoPlan plan_expert_auto(int64_t L, int64_t d, int64_t N, int64_t K, int64_t B, omni_dtype dt);
+// the device's choice of form: gate[1] = distinct experts among a fixed
+// sample of the tasks (auto_sample_size(M) of them), gate[2] = the sample
+// size; bits [ceil(N/32)] uint32 is workspace
+int auto_sample_size(int64_t M);
+hipError_t launch_auto_sample(const int32_t* idx, int M, int64_t N, uint32_t* bits, int32_t* gate,
+                              hipStream_t s);
+hipError_t launch_set_i32(int32_t* p, int v, hipStream_t s);
 hipError_t launch_expert_auto(const void* x, const void* W, const void* V, const int32_t* idx,
                               const float* gate, int L, int d, int64_t N, int K, int B,
                               omni_dtype dt, float* y, int32_t* chosen, const AutoPlan& p,
@@ -313,7 +326,15 @@ hipError_t launch_expert_segments(const int32_t* idx, int N, int32_t* uniq, int3
 // holds (the last step of the backward)
 hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K, omni_dtype dt,
                                    const int32_t* n_uniq, omni_dtype grad_dt, void* dW_rows,
-                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s);
+                                   void* dV_rows, const BwdPlan& p, void* ws, hipStream_t s,
+                                   RunGate run = {});
+// the per-token pass of the per-task backward: dx, dgate and the per-task
+// terms dh, ga (into the plan's workspace); reads n_uniq from the segments
+hipError_t launch_expert_bwd_token(const void* x, const void* W, const void* V,
+                                   const int32_t* idx, const float* gate, const float* dy, int L,
+                                   int d, int K, omni_dtype dt, float* dx, float* dgate,
+                                   const int32_t* n_uniq, const BwdPlan& p, void* ws,
+                                   hipStream_t s, RunGate run = {});
 // dx (expert part, overwritten), dgate, used experts and their dW / dV rows
 hipError_t launch_expert_backward(const void* x, const void* W, const void* V, const int32_t* idx,
                                   const float* gate, const float* dy, int L, int d, int N, int K,
@@ -338,7 +359,27 @@ hipError_t launch_expert_backward_blocked(const void* x, const void* W, const vo
                                           const int32_t* order, int L, int d, int N, int K,
                                           float* dx, float* dgate, int32_t* uniq, int32_t* n_uniq,
                                           omni_dtype grad_dt, void* dW_rows, void* dV_rows,
-                                          const BlockedBwdPlan& p, void* ws, hipStream_t s);
+                                          const BlockedBwdPlan& p, void* ws, hipStream_t s,
+                                          RunGate run = {}, bool segments_done = false);
+
+// the backward in the form the device picks by the forward's rule: the
+// per-task passes, or the blocked form over the token order (tokens sorted
+// by their first expert); both share the sort of the tasks by expert
+struct AutoBwdPlan {
+  BlockedBwdPlan blk;  // with blocked_ok; its per-task plan blk.bwd serves both forms
+  BwdPlan bwd;         // without: the per-task backward alone
+  SchedPlan order_sort;
+  bool blocked_ok;
+  size_t off_flag, off_bits, off_order, off_osort, off_main, ws_bytes;
+};
+AutoBwdPlan plan_expert_backward_auto(int64_t L, int64_t d, int64_t N, int64_t K, omni_dtype dt);
+hipError_t launch_expert_backward_auto(const void* x, const void* W, const void* V,
+                                       const int32_t* idx, const float* gate, const float* dy,
+                                       int L, int d, int N, int K, omni_dtype dt, float* dx,
+                                       float* dgate, int32_t* uniq, int32_t* n_uniq,
+                                       omni_dtype grad_dt, void* dW_rows, void* dV_rows,
+                                       int32_t* chosen, const AutoBwdPlan& p, void* ws,
+                                       hipStream_t s);
 
 struct RouterBwdPlan {
   int Ntot_p, L_p;

@@ -102,6 +102,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_scan_digits(SortJob a, So
                                                                    const int32_t* gate) {
   const bool use_b = gate && auto_choice(gate);
   OMNI_PICK_JOB(j, a, b, use_b);
+  if (j.ntiles == 0) return;  // the empty job of a gated sort
   __shared__ int wsum[SCHED_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = j.ntiles;
@@ -324,6 +325,18 @@ hipError_t sort_dual(const SortSpec& a, const SortSpec& b, const int32_t* gate, 
   return hipGetLastError();
 }
 
+// One sort, run only when the device's choice (run.flag) equals run.want:
+// the other job of the pair is empty (no tiles), so its launches return at
+// once.  Without a gate the sort always runs.
+hipError_t sort_gated(const SortSpec& a, RunGate run, int32_t* chosen, hipStream_t s) {
+  if (!run.flag) return sort_dual(a, a, nullptr, chosen, s);
+  SortSpec none = a;
+  none.M = 0;
+  none.plan.ntiles = 0;
+  return run.want ? sort_dual(none, a, run.flag, chosen, s)
+                  : sort_dual(a, none, run.flag, chosen, s);
+}
+
 hipError_t launch_sched_offsets(const SchedPlan& plan, const void* ws, int M, int G,
                                 int32_t* group_off, hipStream_t s, RunGate run) {
   hipLaunchKernelGGL(sched_offsets, dim3((M + 1 + 255) / 256), dim3(256), 0, s,
@@ -332,17 +345,18 @@ hipError_t launch_sched_offsets(const SchedPlan& plan, const void* ws, int M, in
 }
 
 hipError_t launch_schedule(const int32_t* idx, int M, int B, int G, const SchedPlan& plan,
-                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s) {
+                           int32_t* perm, int32_t* group_off, void* ws, hipStream_t s,
+                           RunGate run) {
   const SortSpec sp{idx, 1, M, B, plan, perm, ws};
-  hipError_t e = sort_dual(sp, sp, nullptr, nullptr, s);
+  hipError_t e = sort_gated(sp, run, nullptr, s);
   if (e != hipSuccess) return e;
-  return launch_sched_offsets(plan, ws, M, G, group_off, s, RunGate{});
+  return launch_sched_offsets(plan, ws, M, G, group_off, s, run);
 }
 
 hipError_t launch_sort_keys(const int32_t* keys, int M, int64_t key_bound, int32_t* order,
-                            void* ws, hipStream_t s) {
+                            void* ws, hipStream_t s, RunGate run) {
   const SortSpec sp{keys, 1, M, 1, plan_schedule(M, 1, key_bound, 1), order, ws};
-  return sort_dual(sp, sp, nullptr, nullptr, s);
+  return sort_gated(sp, run, nullptr, s);
 }
 
 SortSpec token_order_spec(const int32_t* idx, int L, int K, int64_t N, int B, int32_t* order,
@@ -352,9 +366,10 @@ SortSpec token_order_spec(const int32_t* idx, int L, int K, int64_t N, int B, in
 }
 
 hipError_t launch_token_order(const int32_t* idx, int L, int K, int64_t N, int B,
-                              int32_t* order, void* ws, hipStream_t s) {
+                              int32_t* order, void* ws, hipStream_t s, RunGate run,
+                              int32_t* chosen) {
   const SortSpec sp = token_order_spec(idx, L, K, N, B, order, ws);
-  return sort_dual(sp, sp, nullptr, nullptr, s);
+  return sort_gated(sp, run, chosen, s);
 }
 
 }  // namespace omni

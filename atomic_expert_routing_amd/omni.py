@@ -16,17 +16,17 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libomni.so")
-_ABI_VERSION = 9
+_ABI_VERSION = 10
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_UNSUPPORTED, OMNI_ERR_WORKSPACE, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 OMNI_OP_ROUTER, OMNI_OP_SCHEDULE, OMNI_OP_EXPERT_FORWARD = 0, 1, 2
 OMNI_OP_EXPERT_BACKWARD, OMNI_OP_ROUTER_BACKWARD, OMNI_OP_SHARED_MLP = 3, 4, 5
 OMNI_OP_DENSE_ROUTER, OMNI_OP_EXPERT_FORWARD_BLOCKED, OMNI_OP_EXPERT_BACKWARD_BLOCKED = 6, 7, 8
-OMNI_OP_EXPERT_FORWARD_AUTO = 9
+OMNI_OP_EXPERT_FORWARD_AUTO, OMNI_OP_EXPERT_BACKWARD_AUTO = 9, 10
 EXPORTED = ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward", "omni_expert_forward_auto",
             "omni_expert_forward_blocked",
-            "omni_expert_backward_blocked",
+            "omni_expert_backward_blocked", "omni_expert_backward_auto",
             "omni_expert_forward_token_centric", "omni_expert_backward", "omni_router_backward",
             "omni_shared_mlp", "omni_dense_router", "omni_gather_probe", "omni_workspace_bytes",
             "omni_status_string",
@@ -68,6 +68,9 @@ def library() -> ctypes.CDLL:
     lib.omni_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp,
                                          vp, sz, vp]
+    lib.omni_expert_backward_auto.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                              ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                              vp, vp, sz, vp]
     lib.omni_expert_backward_blocked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                  ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp,
                                                  vp, vp, sz, vp]
@@ -82,7 +85,7 @@ def library() -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.POINTER(sz)]
     for f in ("omni_router", "omni_schedule", "omni_schedule_noalloc", "omni_expert_forward",
               "omni_expert_forward_auto", "omni_expert_forward_blocked",
-              "omni_expert_backward_blocked",
+              "omni_expert_backward_blocked", "omni_expert_backward_auto",
               "omni_expert_forward_token_centric", "omni_expert_backward",
               "omni_router_backward", "omni_shared_mlp", "omni_dense_router",
               "omni_gather_probe", "omni_workspace_bytes"):
@@ -337,6 +340,17 @@ def omni_expert_backward(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None,
                             dV_rows, ws, stream, grad_dtype)
 
 
+def omni_expert_backward_auto(x, W, V, idx, gate, dy, dx=None, dgate=None, uniq=None,
+                              n_uniq=None, dW_rows=None, dV_rows=None, ws=None, stream=None,
+                              grad_dtype=torch.float32, chosen=None):
+    """omni_expert_backward in the form the device picks by the forward's
+    rule (per-task, or blocked over the tokens sorted by their first expert);
+    same returns.  chosen (optional [1] int32) receives 1 when the blocked
+    form ran, else 0."""
+    return _expert_backward("auto", x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq, dW_rows,
+                            dV_rows, ws, stream, grad_dtype, chosen)
+
+
 def omni_expert_backward_blocked(x, W, V, idx, gate, dy, token_order, dx=None, dgate=None,
                                  uniq=None, n_uniq=None, dW_rows=None, dV_rows=None, ws=None,
                                  stream=None, grad_dtype=torch.float32):
@@ -347,7 +361,7 @@ def omni_expert_backward_blocked(x, W, V, idx, gate, dy, token_order, dx=None, d
 
 
 def _expert_backward(token_order, x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq, dW_rows,
-                     dV_rows, ws, stream, grad_dtype):
+                     dV_rows, ws, stream, grad_dtype, chosen=None):
     L, d = x.shape
     N = W.shape[0]
     K = idx.shape[1]
@@ -368,10 +382,16 @@ def _expert_backward(token_order, x, W, V, idx, gate, dy, dx, dgate, uniq, n_uni
             _dev(dgate, "dgate", f32, (L, K)), _dev(uniq, "uniq", i32, (cap,)),
             _dev(n_uniq, "n_uniq", i32, (1,)), _dtype_code(dW_rows),
             _dev(dW_rows, "dW_rows", gdt, (cap, d)), _dev(dV_rows, "dV_rows", gdt, (cap, d)))
-    op = OMNI_OP_EXPERT_BACKWARD if token_order is None else OMNI_OP_EXPERT_BACKWARD_BLOCKED
+    auto = isinstance(token_order, str)
+    op = (OMNI_OP_EXPERT_BACKWARD_AUTO if auto else
+          OMNI_OP_EXPERT_BACKWARD if token_order is None else OMNI_OP_EXPERT_BACKWARD_BLOCKED)
     need = omni_workspace_bytes(op, L, d, 1, 1, K, N, 1, dt) if ws is None else 0
     pw, nw = _workspace(ws, need, x.device)
-    if token_order is None:
+    if auto:
+        pc = None if chosen is None else _dev(chosen, "chosen", i32, (1,))
+        _check(library().omni_expert_backward_auto(*args, pc, pw, nw, _stream(stream)),
+               "omni_expert_backward_auto")
+    elif token_order is None:
         _check(library().omni_expert_backward(*args, pw, nw, _stream(stream)),
                "omni_expert_backward")
     else:

@@ -299,6 +299,24 @@ def time_variant(inp, w, br, steps, token_order, assembly, flush):
             "y_bitwise_equal": same, "y_rel_diff": rel}
 
 
+def _median_ms(fn, steps):
+    """Median over `steps` calls of fn, each bracketed by events on the
+    current stream, after one untimed call."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+
 def time_backward(inp, w, br, steps, seed):
     """omni_expert_backward + omni_router_backward on the step's routing, for a
     seeded upstream gradient; preallocated outputs and workspaces.  The expert
@@ -366,18 +384,20 @@ def time_backward(inp, w, br, steps, seed):
             omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
                                               order, dx, dgate, uniq, n_uniq, dW, dV, ws_b)
 
-        run_blocked()
-        torch.cuda.synchronize()
-        tb = []
-        for _ in range(steps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            run_blocked()
-            e1.record()
-            tb.append((e0, e1))
-        torch.cuda.synchronize()
-        blocked_ms = statistics.median(a.elapsed_time(b) for a, b in tb)
+        blocked_ms = _median_ms(run_blocked, steps)
         del ws_b
+    # the automatic backward: the device picks the form by the forward's rule
+    ws_a = torch.empty(omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, L, d, 1, 1, K,
+                                                 N, 1, dt), dtype=torch.uint8, device="cuda")
+    chosen = torch.empty((1,), dtype=i32, device="cuda")
+
+    def run_auto():
+        omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy, dx,
+                                       dgate, uniq, n_uniq, dW, dV, ws_a, chosen=chosen)
+
+    auto_ms = _median_ms(run_auto, steps)
+    auto_chosen = int(chosen.item())
+    del ws_a
     U = int(n_uniq.item())
     es = 2 if w.dtype == "bf16" else 4
     # unique W and V rows read, their fp32 dW and dV rows written; x and dy
@@ -389,6 +409,8 @@ def time_backward(inp, w, br, steps, seed):
         "expert_backward_ms": round(exp_ms, 4),
         "expert_backward_bf16_rows_ms": round(exp16_ms, 4),
         "expert_backward_blocked_ms": None if blocked_ms is None else round(blocked_ms, 4),
+        "expert_backward_auto_ms": round(auto_ms, 4),
+        "expert_backward_auto_chosen": "blocked" if auto_chosen else "per_task",
         "expert_backward_bf16_rows_hbm_frac": round(
             exp16_bytes / (exp16_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "router_backward_ms": round(rt_ms, 4),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define OMNI_ABI_VERSION 9
+#define OMNI_ABI_VERSION 10
 
 #if defined(__GNUC__) || defined(__clang__)
 #define OMNI_API __attribute__((visibility("default")))
@@ -78,7 +78,8 @@ typedef enum {
   OMNI_OP_DENSE_ROUTER = 6,
   OMNI_OP_EXPERT_FORWARD_BLOCKED = 7,
   OMNI_OP_EXPERT_BACKWARD_BLOCKED = 8,
-  OMNI_OP_EXPERT_FORWARD_AUTO = 9
+  OMNI_OP_EXPERT_FORWARD_AUTO = 9,
+  OMNI_OP_EXPERT_BACKWARD_AUTO = 10
 } omni_op;
 
 /* Compiled limits (OMNI_ERR_UNSUPPORTED beyond them). */
@@ -392,6 +393,40 @@ OMNI_API omni_status omni_expert_backward_blocked(const void* x, const void* W, 
                                                   omni_dtype grad_dt, void* dW_rows,
                                                   void* dV_rows, void* ws, size_t ws_bytes,
                                                   void* stream);
+
+/*
+ * omni_expert_backward_auto - the gradients of omni_expert_backward, in the
+ * form that suits the routing, chosen on the device per call by the rule of
+ * omni_expert_forward_auto (the same sample of the tasks, so on the same idx
+ * both passes of a step take the same form; the host never waits).
+ * Source: as omni_expert_backward; the choice answers the digest's
+ * weaknesses paragraph as omni_expert_forward_auto does.
+ *
+ * When the sampled tasks repeat their experts twice or more on average, the
+ * blocked form runs (omni_expert_backward_blocked) over the tokens stably
+ * sorted by their first expert id; otherwise the per-task form
+ * (omni_expert_backward).  The launches of the form not chosen return at
+ * once.  Both forms share the sort of the tasks by expert.  The outputs are
+ * those of omni_expert_backward (the same layout in both forms), equal up to
+ * the rounding of the form taken.  The blocked form is only considered for
+ * bf16 inputs with d % 256 == 0 and L <= 524288.
+ *
+ *   arguments as for omni_expert_backward, plus
+ *   chosen  [1] int32 out, optional (NULL: not written): 1 when the blocked
+ *           form ran, 0 for the per-task form
+ * Requires what omni_expert_backward requires, and the K ids of each token
+ * distinct (as omni_router returns them).  Workspace
+ * (omni_workspace_bytes(OMNI_OP_EXPERT_BACKWARD_AUTO)): the choice, a bitmap
+ * of N bits, the token order and its sort, and the blocked form's buffers
+ * (which hold the per-task form's).
+ */
+OMNI_API omni_status omni_expert_backward_auto(const void* x, const void* W, const void* V,
+                                               const int32_t* idx, const float* gate,
+                                               const float* dy, int64_t L, int64_t d, int64_t N,
+                                               int64_t K, omni_dtype dt, float* dx, float* dgate,
+                                               int32_t* uniq, int32_t* n_uniq, omni_dtype grad_dt,
+                                               void* dW_rows, void* dV_rows, int32_t* chosen,
+                                               void* ws, size_t ws_bytes, void* stream);
 
 /*
  * omni_router_backward - gradients of the Cartesian Product Router.

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = omni.library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.omni_abi_version() == 9
+    assert lib.omni_abi_version() == 10
 
 
 def test_status_strings():
@@ -104,7 +104,7 @@ def test_schedule_validation():
         with pytest.raises(omni.OmniError):
             omni.omni_workspace_bytes(omni.OMNI_OP_SCHEDULE, **args)
     with pytest.raises(omni.OmniError):
-        omni.omni_workspace_bytes(10)
+        omni.omni_workspace_bytes(11)
 
 
 @pytest.mark.parametrize("B", [2**31, 2**32, 2**32 + 5, 2**62])
@@ -343,6 +343,46 @@ def test_auto_assembly_workspace_and_validation():
     assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
     s = lib.omni_expert_forward_auto(fake, fake, fake, fake, fake, 64, 256, 1024, 16, 16,
                                      omni.OMNI_BF16, fake, None, fake, 16, None)
+    assert s == omni.OMNI_ERR_WORKSPACE
+
+
+def test_auto_backward_workspace_and_validation():
+    """omni_expert_backward_auto: the per-task backward's size rules, a
+    workspace that holds either form (the blocked one holds the per-task
+    one's buffers), and rejections before any launch."""
+    L, d, K, N = 4096, 2048, 128, 1700416
+    auto = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, L=L, d=d, K=K, N=N)
+    blocked = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_BLOCKED, L=L, d=d, K=K, N=N)
+    per_task = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, L=L, d=d, K=K, N=N)
+    assert auto >= blocked + L * 4 and auto >= per_task
+    # fp32 inputs, d % 256 != 0 or L above the blocked form's limit: the
+    # per-task backward alone
+    for kw in (dict(dtype=omni.OMNI_F32), dict(d=2112), dict(L=524288 + 64, K=2)):
+        args = dict(L=L, d=d, K=K, N=N)
+        args.update(kw)
+        alone = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD, **args)
+        got = omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, **args)
+        assert got == (alone + 255) // 256 * 256, kw
+    for kw, st in ((dict(K=513), omni.OMNI_ERR_UNSUPPORTED), (dict(d=12), omni.OMNI_ERR_UNSUPPORTED),
+                   (dict(N=0), omni.OMNI_ERR_INVALID_ARG)):
+        args = dict(L=64, d=256, K=16, N=1024)
+        args.update(kw)
+        with pytest.raises(omni.OmniError) as e:
+            omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, **args)
+        assert e.value.status == st
+    lib = omni.library()
+    fake = ctypes.c_void_p(4096)
+    s = lib.omni_expert_backward_auto(fake, fake, fake, fake, fake, None, 64, 256, 1024, 16,
+                                      omni.OMNI_BF16, fake, fake, fake, fake, omni.OMNI_F32, fake,
+                                      fake, None, fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"NULL" in lib.omni_last_error()
+    s = lib.omni_expert_backward_auto(fake, fake, fake, fake, fake, fake, 64, 256, 1024, 16,
+                                      omni.OMNI_BF16, fake, fake, fake, fake, 7, fake, fake, None,
+                                      fake, 1 << 30, None)
+    assert s == omni.OMNI_ERR_INVALID_ARG and b"grad_dt" in lib.omni_last_error()
+    s = lib.omni_expert_backward_auto(fake, fake, fake, fake, fake, fake, 64, 256, 1024, 16,
+                                      omni.OMNI_BF16, fake, fake, fake, fake, omni.OMNI_F32, fake,
+                                      fake, None, fake, 16, None)
     assert s == omni.OMNI_ERR_WORKSPACE
 
 

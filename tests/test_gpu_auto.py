@@ -141,3 +141,120 @@ def test_auto_graph_replays_switch_form_with_the_inputs():
         torch.cuda.synchronize()
         assert int(br.chosen.item()) == want[name][1], rep
         assert torch.equal(br.y, want[name][0]), rep
+
+
+BLK_BWD_MAX_L = 524288  # tokens the blocked backward's per-token bitmap holds
+
+
+def _bwd_choice(idx, dt, d, L):
+    """The backward's rule: the forward's, within the blocked backward's own
+    limit on L."""
+    return int(expected_choice(idx, dt, d) and L <= BLK_BWD_MAX_L)
+
+
+def _assert_same_backward(got, ref, n):
+    assert int(got[3].item()) == n and torch.equal(got[2][:n], ref[2][:n])
+    for name, a, b in (("dx", got[0], ref[0]), ("dgate", got[1], ref[1]),
+                       ("dW", got[4][:n], ref[4][:n]), ("dV", got[5][:n], ref[5][:n])):
+        assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "L{}_d{}_{}x{}_K{}_B{}_{}_{}".format(*c))
+def test_auto_backward_takes_the_expected_form(case):
+    """omni_expert_backward_auto on the oracle's routing: the flag follows the
+    forward's rule, every output equals the chosen form's bit for bit, and
+    the gradients meet the backward oracle (fp32-arithmetic bound)."""
+    from oracle import omni_backward_oracle as BO
+    L, d, Nr, Nc, K, B, dt, dist = case
+    w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, B, dt, x_dist=dist,
+                                 seed=zlib.crc32(repr(case).encode()) % 1000)
+    say(f"auto backward {w.name} ({dist})")
+    idx_o, _, gate_o, _, _ = O.route(inp_cpu["x"], inp_cpu["Wr"], inp_cpu["Wc"], K)
+    inp = {k: v.cuda() for k, v in inp_cpu.items()}
+    idx = torch.as_tensor(idx_o, dtype=torch.int32).cuda()
+    gate = torch.as_tensor(gate_o, dtype=torch.float32).cuda()
+    dy = synth.upstream_grad(w, seed=3).cuda()
+    chosen = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    got = omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], idx, gate, dy,
+                                         chosen=chosen)
+    torch.cuda.synchronize()
+    want = _bwd_choice(idx, dt, d, L)
+    assert int(chosen.item()) == want
+    if want == 0:
+        ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], idx, gate, dy)
+    else:
+        order = omni.omni_schedule(idx, w.N, 1, token_order=True, tasks=False)[2]
+        ref = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], idx, gate, dy,
+                                                order)
+    torch.cuda.synchronize()
+    n = int(ref[3].item())
+    _assert_same_backward(got, ref, n)
+    gate_f = to_np(gate).astype(np.float64)
+    dy_c = to_np(dy).astype(np.float64)
+    terms = BO.task_terms(inp_cpu["x"], inp_cpu["W"], inp_cpu["V"], idx_o, gate_f, dy_c)
+    assert np.array_equal(to_np(got[2])[:n], np.unique(idx_o))
+    dW_o, dV_o = BO.expert_grads(inp_cpu["x"], dy_c, idx_o, terms, np.unique(idx_o))
+    dx_o = BO.input_grad_expert(inp_cpu["W"], idx_o, terms["dh"])
+    errs = {"dgate": check_y(got[1], terms["dgate"].reshape(L, K), RTOL_FP32_ARITH),
+            "dx": check_y(got[0], dx_o, RTOL_FP32_ARITH),
+            "dW": check_y(to_np(got[4])[:n], dW_o, RTOL_FP32_ARITH),
+            "dV": check_y(to_np(got[5])[:n], dV_o, RTOL_FP32_ARITH)}
+    say(f"  chosen={want} " + " ".join(f"{k}={v[0]:.1e}" for k, v in errs.items()))
+
+
+def test_auto_backward_one_workspace_serves_both_forms():
+    """One workspace, clustered then spread-out then clustered routing: each
+    call takes its own form and equals that form's output bit for bit."""
+    L, d, Nr, Nc, K, B = 512, 256, 128, 128, 16, 16
+    ws = torch.empty((omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, L=L, d=d,
+                                                K=K, N=Nr * Nc),), dtype=torch.uint8,
+                     device="cuda")
+    chosen = torch.empty((1,), dtype=torch.int32, device="cuda")
+    for rep, dist in enumerate(("clustered", "normal", "clustered")):
+        w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, B, "bf16", x_dist=dist, seed=60 + rep)
+        inp = {k: v.cuda() for k, v in inp_cpu.items()}
+        br = omni.RoutedBranch(L, d, Nr, Nc, K, B, torch.bfloat16)
+        br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+        dy = synth.upstream_grad(w, seed=rep).cuda()
+        say(f"auto backward, shared workspace: call {rep} ({dist})")
+        got = omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                             ws=ws, chosen=chosen)
+        torch.cuda.synchronize()
+        assert int(chosen.item()) == int(br.chosen.item()) == (1 if dist == "clustered" else 0)
+        if dist == "clustered":
+            order = omni.omni_schedule(br.idx, w.N, 1, token_order=True, tasks=False)[2]
+            ref = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], br.idx,
+                                                    br.gate, dy, order)
+        else:
+            ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy)
+        torch.cuda.synchronize()
+        _assert_same_backward(got, ref, int(ref[3].item()))
+
+
+@pytest.mark.parametrize("name", ["skewed_L16384_N1700416_d2048", synth.HEADLINE])
+def test_auto_backward_full_size(name):
+    """Both full-size workloads: the skewed one takes the blocked form, the
+    spread-out one the per-task form, each bit for bit."""
+    w = synth.WORKLOADS[name]
+    say(f"auto backward full-size {name}")
+    inp = synth.make_inputs(w, seed=0, device="cuda")
+    br = omni.RoutedBranch(w.L, w.d, w.Nr, w.Nc, w.K, w.B, w.torch_dtype)
+    br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    dy = synth.upstream_grad(w, seed=0, device="cuda")
+    chosen = torch.empty((1,), dtype=torch.int32, device="cuda")
+    got = omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                         chosen=chosen)
+    torch.cuda.synchronize()
+    want = _bwd_choice(br.idx, w.dtype, w.d, w.L)
+    assert int(chosen.item()) == want == int(br.chosen.item())
+    assert want == (1 if name.startswith("skewed") else 0)
+    if want:
+        order = omni.omni_schedule(br.idx, w.N, 1, token_order=True, tasks=False)[2]
+        ref = omni.omni_expert_backward_blocked(inp["x"], inp["W"], inp["V"], br.idx, br.gate,
+                                                dy, order)
+    else:
+        ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy)
+    torch.cuda.synchronize()
+    _assert_same_backward(got, ref, int(ref[3].item()))
+    del inp, br, got, ref
+    torch.cuda.empty_cache()
