@@ -69,6 +69,25 @@ __device__ __forceinline__ u32x4 ld16_nt(const char* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
+// A buffer resource spanning one row of `bytes` bytes: its loads take the
+// row's base from scalar registers, and a load past the row's end returns
+// zero (the ragged last 1 KB chunk of a row needs no test).  Word 3 selects
+// the 32-bit data format; a zero format would make every untyped load
+// return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)bytes, 0x00020000);
+}
+// Cache policies of the buffer loads (the instruction's cache-policy field):
+// plain, or non-temporal (streamed: the line is not kept for reuse).
+constexpr int LD_PLAIN = 0, LD_NT = 2;
+
+// Chunk c (1 KB) of a row through its buffer resource: lane l's 16 bytes at
+// c * 1024 + 16 l.
+template <int POLICY>
+__device__ __forceinline__ u32x4 ld_row16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
+}
+
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float uni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
@@ -94,8 +113,13 @@ __device__ __forceinline__ float uni(float v) {
 // the next task is in flight while the current one is reduced (two row
 // buffers).  Measured on the 4096-token, 1.7M-expert workload: chunks of 8
 // to 32 tasks are equally fast and 128 is 10% slower; without the XCD split
-// the x rows fall out of L2 and the pass is 15% slower; plain loads of W
-// beat non-temporal ones (repeated experts of a group hit in the caches).
+// the x rows fall out of L2 and the pass is 15% slower.
+// Both rows are buffer loads (scalar row base); the W rows are
+// non-temporal, so the stream of W rows, each used by about one task, does
+// not push the XCD's x rows out of L2.  Per-task call (act_plan, this pass,
+// the output pass), against plain global loads: 815 -> 791 us at 4096
+// tokens x 1.7M experts, 430 -> 418 us at 1M, 191 -> 172 us at 280,900
+// (the same y bit for bit).
 constexpr int ACT_CHUNK = 32;
 constexpr int XCDS = 8;
 constexpr int ACT_MAX_CHUNK_GROUPS = 16384;
@@ -148,20 +172,14 @@ __global__ __launch_bounds__(64) void expert_act(const uint16_t* __restrict__ x_
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   const unsigned cb = lane * 16u;
   auto load_x = [&](int t, u32x4* r) {
-    const char* base = (const char*)x_ + (size_t)t * row_bytes;
+    const auto rs = row_rsrc((const char*)x_ + (size_t)t * row_bytes, row_bytes);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const unsigned o = c * 1024u + cb;
-      r[c] = o < row_bytes ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < NCH; ++c) r[c] = ld_row16<LD_PLAIN>(rs, c * 1024u + cb);
   };
   auto load_w = [&](int e, u32x4* r) {
-    const char* base = (const char*)W_ + (size_t)e * row_bytes;
+    const auto rs = row_rsrc((const char*)W_ + (size_t)e * row_bytes, row_bytes);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const unsigned o = c * 1024u + cb;
-      r[c] = o < row_bytes ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < NCH; ++c) r[c] = ld_row16<LD_NT>(rs, c * 1024u + cb);
   };
   // grid-stride over the chunks: workgroup 8j + x takes chunks j, j + G, ...
   // (G = gridDim / 8) for token class x
@@ -362,8 +380,9 @@ __global__ __launch_bounds__(256) void expert_out_w(const uint16_t* __restrict__
 // ablation that reverts expert-centric scheduling): each token fetches the
 // rows of its own K experts, with no schedule.  One workgroup per token:
 // wave w computes a_k = g_k * SiLU(x_t . W[e_k]) for k = w, w+4, ... (x_t held
-// in registers, TC_ROWS W rows in flight), the K activations meet in LDS, and
-// the V pass is the one of expert_out (one workgroup per token).
+// in registers, TC_ROWS W rows in flight, loaded as in expert_act: buffer
+// loads, non-temporal), the K activations meet in LDS, and the V pass is the
+// one of expert_out (one workgroup per token).
 constexpr int TC_ROWS = 4;
 
 template <bool BF16, int NCH>
@@ -399,12 +418,11 @@ __global__ __launch_bounds__(256) void expert_tc(const uint16_t* __restrict__ x_
 #pragma unroll
     for (int q = 0; q < TC_ROWS; ++q) {
       const int k = k0 + 4 * q;
-      const char* base = (const char*)W_ + (size_t)uni(se[k < K ? k : k0]) * row_bytes;
+      // rows past K: an empty buffer, whose loads return zero
+      const auto rs = row_rsrc((const char*)W_ + (size_t)uni(se[k < K ? k : k0]) * row_bytes,
+                               k < K ? row_bytes : 0u);
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const unsigned o = c * 1024u + cb;
-        w[q][c] = (k < K && o < row_bytes) ? *(const u32x4*)(base + o) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int c = 0; c < NCH; ++c) w[q][c] = ld_row16<LD_NT>(rs, c * 1024u + cb);
     }
 #pragma unroll
     for (int q = 0; q < TC_ROWS; ++q) {
