@@ -18,14 +18,16 @@
 //   seg_count/scan/write  the tasks sorted by expert id (the schedule with
 //                      groups of one expert) are cut into per-expert
 //                      segments: list of used experts and segment starts.
-//   expert_bwd_token   one workgroup per token: its K (W, V) rows give h and u;
+//   expert_bwd_token   one workgroup per token (the grid strides over the
+//                      tokens beyond 8192): its K (W, V) rows give h and u;
 //                      dgate, dh, ga per task and the token-owned dx_t.
 //   row_keys, a radix sort, row_recs
 //                      the used experts ordered for the row pass: by the
 //                      XCD class t % 8 of their first task's token t, then
 //                      by t, dealt out so that workgroup b (on XCD b % 8)
 //                      mostly takes an expert of class b % 8.
-//   expert_bwd_rows    one workgroup per used expert: dW and dV rows summed
+//   expert_bwd_rows    one workgroup per used expert (the grid strides over
+//                      them beyond 32768): dW and dV rows summed
 //                      over the expert's tasks in (token, k) order, written
 //                      once, no atomics (each row has one owner).
 //   router_bwd_ds      one workgroup per token: dS and the token's ds row
@@ -76,128 +78,138 @@ __device__ __forceinline__ float silu_grad(float h, float sg) { return sg * (1.f
 // flight.  dx_t is summed per wave in registers, then over the 4 waves in
 // LDS in wave order.
 constexpr int BWD_WAVES = 4;
+// Grid bounds of the per-task kernels, which stride over their tokens or
+// used experts: the workgroups of the form not chosen by the automatic
+// backward only read the choice and leave, and their dispatch costs time in
+// proportion to their number.
+constexpr int BWD_TOKEN_GRID = 8192;
+constexpr int BWD_ROWS_GRID = 32768;  // a multiple of 8
 
 template <bool BF16, int NCH>
 __global__ __launch_bounds__(256) void expert_bwd_token(
     const uint16_t* __restrict__ x_, const uint16_t* __restrict__ W_, const uint16_t* __restrict__ V_,
     const int32_t* __restrict__ idx, const float* __restrict__ gate, const float* __restrict__ dy,
-    const int32_t* __restrict__ n_uniq, int d, int K, float* __restrict__ dx,
+    const int32_t* __restrict__ n_uniq, int L, int d, int K, float* __restrict__ dx,
     float* __restrict__ dgate, float* __restrict__ dh_out, float* __restrict__ ga_out,
     const int32_t* run_flag, int run_want) {
   if (gated_out(run_flag, run_want)) return;
   using C = Chunk<BF16>;
   constexpr int E = C::E;
   extern __shared__ __attribute__((aligned(16))) float red[];  // [BWD_WAVES][d]
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   const int nchunk = (int)(row_bytes / 16);
 
-  float xr[NCH][E], dyr[NCH][E], acc[NCH][E];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = lane + 64 * j;
-    const bool in = c < nchunk;
-    u32x4 v = in ? *(const u32x4*)((const char*)x_ + (size_t)t * row_bytes + c * 16u)
-                 : u32x4{0u, 0u, 0u, 0u};
-    C::widen(v, xr[j]);
-    const float* dyp = dy + (size_t)t * d + c * E;
-#pragma unroll
-    for (int q = 0; q < E; q += 4) {
-      const f32x4 f = in ? *(const f32x4*)(dyp + q) : f32x4{0.f, 0.f, 0.f, 0.f};
-      dyr[j][q] = f[0]; dyr[j][q + 1] = f[1]; dyr[j][q + 2] = f[2]; dyr[j][q + 3] = f[3];
-    }
-#pragma unroll
-    for (int q = 0; q < E; ++q) acc[j][q] = 0.f;
-  }
-
-  // Rows used by fewer than two tasks on average (used experts, counted by
-  // the sort that ran before this kernel, above half the task count) are
-  // loaded non-temporally: 4096 tokens x 1.7M experts (1.17 tasks per used
-  // expert) 2.46 -> 2.38 ms for the whole call.  With reuse the plain loads
-  // let repeated rows hit the caches (16384 clustered tokens, 167 tasks per
-  // expert: 11.6 ms plain against 13.5 ms non-temporal).
-  const bool stream_rows = 2ll * n_uniq[0] > (long long)gridDim.x * K;
-  auto load_rows = [&](int k, u32x4* w, u32x4* v) {
-    const bool live = k < K;
-    const int e = live ? uni(idx[(size_t)t * K + k]) : 0;
-    const char* wb = (const char*)W_ + (size_t)e * row_bytes;
-    const char* vb = (const char*)V_ + (size_t)e * row_bytes;
-    if (stream_rows) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int c = lane + 64 * j;
-        const bool in = live && c < nchunk;
-        w[j] = in ? __builtin_nontemporal_load((const u32x4*)(wb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
-        v[j] = in ? __builtin_nontemporal_load((const u32x4*)(vb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int c = lane + 64 * j;
-        const bool in = live && c < nchunk;
-        w[j] = in ? *(const u32x4*)(wb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
-        v[j] = in ? *(const u32x4*)(vb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto task = [&](int k, const u32x4* w, const u32x4* v) {
-    float wf[NCH][E];
-    float ph = 0.f, pu = 0.f;
+  // workgroup b takes tokens b, b + grid, ... (one each up to the grid bound)
+  for (int t = blockIdx.x; t < L; t += gridDim.x) {
+    float xr[NCH][E], dyr[NCH][E], acc[NCH][E];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      float vf[E];
-      C::widen(w[j], wf[j]);
-      C::widen(v[j], vf);
+      const int c = lane + 64 * j;
+      const bool in = c < nchunk;
+      u32x4 v = in ? *(const u32x4*)((const char*)x_ + (size_t)t * row_bytes + c * 16u)
+                   : u32x4{0u, 0u, 0u, 0u};
+      C::widen(v, xr[j]);
+      const float* dyp = dy + (size_t)t * d + c * E;
 #pragma unroll
-      for (int q = 0; q < E; ++q) {
-        ph = fmaf(xr[j][q], wf[j][q], ph);
-        pu = fmaf(dyr[j][q], vf[q], pu);
+      for (int q = 0; q < E; q += 4) {
+        const f32x4 f = in ? *(const f32x4*)(dyp + q) : f32x4{0.f, 0.f, 0.f, 0.f};
+        dyr[j][q] = f[0]; dyr[j][q + 1] = f[1]; dyr[j][q + 2] = f[2]; dyr[j][q + 3] = f[3];
+      }
+#pragma unroll
+      for (int q = 0; q < E; ++q) acc[j][q] = 0.f;
+    }
+
+    // Rows used by fewer than two tasks on average (used experts, counted by
+    // the sort that ran before this kernel, above half the task count) are
+    // loaded non-temporally: 4096 tokens x 1.7M experts (1.17 tasks per used
+    // expert) 2.46 -> 2.38 ms for the whole call.  With reuse the plain loads
+    // let repeated rows hit the caches (16384 clustered tokens, 167 tasks per
+    // expert: 11.6 ms plain against 13.5 ms non-temporal).
+    const bool stream_rows = 2ll * n_uniq[0] > (long long)L * K;
+    auto load_rows = [&](int k, u32x4* w, u32x4* v) {
+      const bool live = k < K;
+      const int e = live ? uni(idx[(size_t)t * K + k]) : 0;
+      const char* wb = (const char*)W_ + (size_t)e * row_bytes;
+      const char* vb = (const char*)V_ + (size_t)e * row_bytes;
+      if (stream_rows) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const int c = lane + 64 * j;
+          const bool in = live && c < nchunk;
+          w[j] = in ? __builtin_nontemporal_load((const u32x4*)(wb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
+          v[j] = in ? __builtin_nontemporal_load((const u32x4*)(vb + c * 16u)) : u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const int c = lane + 64 * j;
+          const bool in = live && c < nchunk;
+          w[j] = in ? *(const u32x4*)(wb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
+          v[j] = in ? *(const u32x4*)(vb + c * 16u) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    auto task = [&](int k, const u32x4* w, const u32x4* v) {
+      float wf[NCH][E];
+      float ph = 0.f, pu = 0.f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        float vf[E];
+        C::widen(w[j], wf[j]);
+        C::widen(v[j], vf);
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          ph = fmaf(xr[j][q], wf[j][q], ph);
+          pu = fmaf(dyr[j][q], vf[q], pu);
+        }
+      }
+      const float h = wave_sum(ph), u = wave_sum(pu);
+      const size_t m = (size_t)t * K + k;
+      const float g = uni(gate[m]);
+      const float sg = 1.f / (1.f + expf(-h));
+      const float a = h * sg;
+      const float dh = g * u * silu_grad(h, sg);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int q = 0; q < E; ++q) acc[j][q] = fmaf(dh, wf[j][q], acc[j][q]);
+      if (lane == 0) {
+        dgate[m] = a * u;
+        dh_out[m] = dh;
+        ga_out[m] = g * a;
+      }
+    };
+    u32x4 wa[NCH], va[NCH], wb[NCH], vb[NCH];
+    load_rows(wave, wa, va);
+    for (int k = wave; k < K; k += 2 * BWD_WAVES) {
+      load_rows(k + BWD_WAVES, wb, vb);
+      task(k, wa, va);
+      if (k + BWD_WAVES < K) {
+        load_rows(k + 2 * BWD_WAVES, wa, va);
+        task(k + BWD_WAVES, wb, vb);
       }
     }
-    const float h = wave_sum(ph), u = wave_sum(pu);
-    const size_t m = (size_t)t * K + k;
-    const float g = uni(gate[m]);
-    const float sg = 1.f / (1.f + expf(-h));
-    const float a = h * sg;
-    const float dh = g * u * silu_grad(h, sg);
+    // dx_t: per-wave partial sums meet in LDS, added in wave order
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk)
 #pragma unroll
-      for (int q = 0; q < E; ++q) acc[j][q] = fmaf(dh, wf[j][q], acc[j][q]);
-    if (lane == 0) {
-      dgate[m] = a * u;
-      dh_out[m] = dh;
-      ga_out[m] = g * a;
+        for (int q = 0; q < E; ++q) red[wave * d + c * E + q] = acc[j][q];
     }
-  };
-  u32x4 wa[NCH], va[NCH], wb[NCH], vb[NCH];
-  load_rows(wave, wa, va);
-  for (int k = wave; k < K; k += 2 * BWD_WAVES) {
-    load_rows(k + BWD_WAVES, wb, vb);
-    task(k, wa, va);
-    if (k + BWD_WAVES < K) {
-      load_rows(k + 2 * BWD_WAVES, wa, va);
-      task(k + BWD_WAVES, wb, vb);
+    __syncthreads();
+    for (int col = tid * 4; col < d; col += 256 * 4) {
+      f32x4 s = *(const f32x4*)(red + col);
+#pragma unroll
+      for (int w = 1; w < BWD_WAVES; ++w) {
+        const f32x4 o = *(const f32x4*)(red + w * d + col);
+        s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+      }
+      *(f32x4*)(dx + (size_t)t * d + col) = s;
     }
-  }
-  // dx_t: per-wave partial sums meet in LDS, added in wave order
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nchunk)
-#pragma unroll
-      for (int q = 0; q < E; ++q) red[wave * d + c * E + q] = acc[j][q];
-  }
-  __syncthreads();
-  for (int col = tid * 4; col < d; col += 256 * 4) {
-    f32x4 s = *(const f32x4*)(red + col);
-#pragma unroll
-    for (int w = 1; w < BWD_WAVES; ++w) {
-      const f32x4 o = *(const f32x4*)(red + w * d + col);
-      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
-    }
-    *(f32x4*)(dx + (size_t)t * d + col) = s;
+    __syncthreads();  // red is written again for the next token
   }
 }
 
@@ -413,52 +425,54 @@ __global__ __launch_bounds__(512) void expert_bwd_rows(
   if (gated_out(run_flag, run_want)) return;
   using C = Chunk<BF16>;
   constexpr int E = C::E;
-  const int b = blockIdx.x;
-  // rec has a slot for every workgroup (the grid is the used-expert bound):
-  // both loads are issued together, and slots past n_uniq are never used
-  const int n = n_uniq[0];
-  const int4 rc = rec[b];
-  if (b >= n) return;
-  const int r = uni(rc.x), s0 = uni(rc.y), s1 = uni(rc.z), m0 = uni(rc.w);
   const int c = threadIdx.x;
   const unsigned row_bytes = (unsigned)d * (BF16 ? 2u : 4u);
   if (c * 16u >= row_bytes) return;  // no barrier below
-  float aw[E], av[E];
+  // Workgroup b takes used experts b, b + grid, ...  The first record is
+  // loaded beside the count (slot blockIdx.x exists: the grid is at most the
+  // used-expert bound, the length of rec); slots past n_uniq are never used.
+  const int n = n_uniq[0];
+  int4 rc = rec[blockIdx.x];
+  for (int b = blockIdx.x; b < n; b += gridDim.x) {
+    if (b != (int)blockIdx.x) rc = rec[b];
+    const int r = uni(rc.x), s0 = uni(rc.y), s1 = uni(rc.z), m0 = uni(rc.w);
+    float aw[E], av[E];
 #pragma unroll
-  for (int q = 0; q < E; ++q) aw[q] = av[q] = 0.f;
-  auto load = [&](int p, u32x4& xv, f32x4* dv, float& sdh, float& sga) {
-    const int m = p == s0 ? m0 : uni(perm[p]);
-    const int t = m / K;
-    sdh = uni(dh[m]);
-    sga = uni(ga[m]);
-    xv = *(const u32x4*)((const char*)x_ + (size_t)t * row_bytes + c * 16u);
-    const float* dyp = dy + (size_t)t * d + c * E;
+    for (int q = 0; q < E; ++q) aw[q] = av[q] = 0.f;
+    auto load = [&](int p, u32x4& xv, f32x4* dv, float& sdh, float& sga) {
+      const int m = p == s0 ? m0 : uni(perm[p]);
+      const int t = m / K;
+      sdh = uni(dh[m]);
+      sga = uni(ga[m]);
+      xv = *(const u32x4*)((const char*)x_ + (size_t)t * row_bytes + c * 16u);
+      const float* dyp = dy + (size_t)t * d + c * E;
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) dv[q] = *(const f32x4*)(dyp + 4 * q);
-  };
-  u32x4 xa, xb;
-  f32x4 da[E / 4], db[E / 4];
-  float ha, gaa, hb, gab;
-  auto accum = [&](const u32x4 xv, const f32x4* dv, float sdh, float sga) {
-    float xf[E];
-    C::widen(xv, xf);
+      for (int q = 0; q < E / 4; ++q) dv[q] = *(const f32x4*)(dyp + 4 * q);
+    };
+    u32x4 xa, xb;
+    f32x4 da[E / 4], db[E / 4];
+    float ha, gaa, hb, gab;
+    auto accum = [&](const u32x4 xv, const f32x4* dv, float sdh, float sga) {
+      float xf[E];
+      C::widen(xv, xf);
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
-      aw[q] = fmaf(sdh, xf[q], aw[q]);
-      av[q] = fmaf(sga, dv[q / 4][q % 4], av[q]);
+      for (int q = 0; q < E; ++q) {
+        aw[q] = fmaf(sdh, xf[q], aw[q]);
+        av[q] = fmaf(sga, dv[q / 4][q % 4], av[q]);
+      }
+    };
+    load(s0, xa, da, ha, gaa);
+    for (int p = s0; p < s1; p += 2) {
+      if (p + 1 < s1) load(p + 1, xb, db, hb, gab);
+      accum(xa, da, ha, gaa);
+      if (p + 1 < s1) {
+        if (p + 2 < s1) load(p + 2, xa, da, ha, gaa);
+        accum(xb, db, hb, gab);
+      }
     }
-  };
-  load(s0, xa, da, ha, gaa);
-  for (int p = s0; p < s1; p += 2) {
-    if (p + 1 < s1) load(p + 1, xb, db, hb, gab);
-    accum(xa, da, ha, gaa);
-    if (p + 1 < s1) {
-      if (p + 2 < s1) load(p + 2, xa, da, ha, gaa);
-      accum(xb, db, hb, gab);
-    }
+    store_row_chunk<OUT_BF16, E>(dW_rows, (size_t)r, d, c, aw);
+    store_row_chunk<OUT_BF16, E>(dV_rows, (size_t)r, d, c, av);
   }
-  store_row_chunk<OUT_BF16, E>(dW_rows, (size_t)r, d, c, aw);
-  store_row_chunk<OUT_BF16, E>(dV_rows, (size_t)r, d, c, av);
 }
 
 // ------------------------------------------------------------------ router_bwd_ds
@@ -595,10 +609,11 @@ hipError_t launch_bwd_token_t(const void* x, const void* W, const void* V, const
   const int nch = (int)(((size_t)d * (BF16 ? 2 : 4) / 16 + 63) / 64);
   const size_t lds = (size_t)BWD_WAVES * d * 4;
   const uint16_t *xp = (const uint16_t*)x, *wp = (const uint16_t*)W, *vp = (const uint16_t*)V;
+  const dim3 grid((unsigned)std::min(L, BWD_TOKEN_GRID));
 #define OMNI_BT(N)                                                                            \
   case N:                                                                                     \
-    hipLaunchKernelGGL((expert_bwd_token<BF16, N>), dim3(L), dim3(256), lds, s, xp, wp, vp, idx, \
-                       gate, dy, n_uniq, d, K, dx, dgate, dh, ga, run.flag, run.want);        \
+    hipLaunchKernelGGL((expert_bwd_token<BF16, N>), grid, dim3(256), lds, s, xp, wp, vp, idx,  \
+                       gate, dy, n_uniq, L, d, K, dx, dgate, dh, ga, run.flag, run.want);     \
     break;
   switch (nch) {
     OMNI_BT(1) OMNI_BT(2) OMNI_BT(3) OMNI_BT(4) OMNI_BT(5) OMNI_BT(6) OMNI_BT(7) OMNI_BT(8)
@@ -715,7 +730,11 @@ hipError_t launch_expert_grad_rows(const void* x, const float* dy, int d, int K,
   const bool bf = dt == OMNI_BF16;
   const int E = bf ? 8 : 4;
   const int threads = ((d / E + 63) / 64) * 64;  // <= 512 for the supported d
-  const dim3 grid((unsigned)p.U_max);
+  // a bounded grid (a multiple of 8, so that slot b keeps its XCD b % 8 in
+  // every round): with the blocked form chosen, these workgroups only read
+  // the choice and leave, and one per possible used expert (1.7M on the
+  // skewed workload) took 0.4 ms just to dispatch
+  const dim3 grid((unsigned)std::min(p.U_max, BWD_ROWS_GRID));
   const bool obf = grad_dt == OMNI_BF16;
 #define OMNI_ROWS(IB, OB)                                                                        \
   hipLaunchKernelGGL((expert_bwd_rows<IB, OB>), grid, dim3(threads), 0, s, (const uint16_t*)x, dy, \

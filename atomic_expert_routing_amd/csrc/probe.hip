@@ -10,11 +10,16 @@
 namespace omni {
 namespace {
 
-constexpr int PROBE_ROWS = 4;  // rows in flight per wave
+constexpr int PROBE_ROWS = 8;  // rows in flight per wave
 
 // Wave w of the grid reads rows w, w + waves, ... of the list, each row as
 // 16-byte chunks spread over the 64 lanes, PROBE_ROWS rows at a time, and
-// stores one checksum per lane so that no load is dead.
+// stores one checksum per lane so that no load is dead.  The loads are
+// non-temporal, the fastest form measured for rows read once: the 447,367
+// used rows (4 KB each) of the 4096-token, 1.7M-expert step gather at
+// 6.1 TB/s this way against 4.8 TB/s with plain loads (buffer loads and 4 to
+// 16 rows in flight within 2%); the used 1.5 KB rows at 280,900 experts at
+// 4.7 against 2.4 TB/s.
 __global__ __launch_bounds__(256) void gather_rows(const unsigned char* __restrict__ A,
                                                    int64_t nA, const int32_t* __restrict__ rows,
                                                    int64_t n, int row_bytes,
@@ -33,7 +38,8 @@ __global__ __launch_bounds__(256) void gather_rows(const unsigned char* __restri
         const int64_t r = r0 + j;
         const int64_t row = r < n ? rows[r] : -1;  // ids outside [0, nA) are skipped
         v[j] = (row >= 0 && row < nA && c < chunks)
-                   ? *(const u32x4*)(A + (size_t)row * (size_t)row_bytes + (size_t)c * 16)
+                   ? __builtin_nontemporal_load(
+                         (const u32x4*)(A + (size_t)row * (size_t)row_bytes + (size_t)c * 16))
                    : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll

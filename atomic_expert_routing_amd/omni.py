@@ -462,7 +462,7 @@ def omni_gather_probe(A, rows, sink=None, stream=None):
     assembly's access pattern; returns the checksum sink."""
     n = rows.numel()
     row_bytes = A.shape[1] * A.element_size()
-    need = 256 * min(8192, max(1, -(-n // 16)))
+    need = 256 * min(8192, max(1, -(-n // 32)))
     sink = torch.empty(need, dtype=torch.float32, device=A.device) if sink is None else sink
     _check(library().omni_gather_probe(_dev(A, "A"), A.shape[0], row_bytes,
                                        _dev(rows, "rows", torch.int32), n,

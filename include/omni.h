@@ -507,12 +507,13 @@ OMNI_API omni_status omni_dense_router(const void* x, const void* Wn, int64_t L,
 /*
  * omni_gather_probe - measurement aid, not part of the method: reads the
  * listed rows of a row-major matrix A [n_rows_A, row_bytes] in random order
- * (one wave per row, four rows in flight), as the expert assembly reads the
- * rows of W and V, and writes a checksum per thread to sink.  Timed on the
+ * (one wave per row, eight rows in flight, non-temporal loads), as the
+ * expert assembly reads the rows of W and V, and writes a checksum per
+ * thread to sink.  Timed on the
  * rows a step uses, it gives the gather rate the memory system delivers for
  * that pattern, beside the nominal HBM peak.
  *   rows  [n] int32   row ids; ids outside [0, n_rows_A) are skipped
- *   sink  [sink_floats] fp32 out, at least 256 * min(8192, ceil(n / 16))
+ *   sink  [sink_floats] fp32 out, at least 256 * min(8192, ceil(n / 32))
  * Requires row_bytes a multiple of 16 in [16, 65536].
  */
 OMNI_API omni_status omni_gather_probe(const void* A, int64_t n_rows_A, int64_t row_bytes,
