@@ -258,3 +258,66 @@ def test_auto_backward_full_size(name):
     _assert_same_backward(got, ref, int(ref[3].item()))
     del inp, br, got, ref
     torch.cuda.empty_cache()
+
+
+def test_auto_backward_graph_replays_switch_form_with_the_inputs():
+    """A captured automatic backward replays correctly on routing of either
+    kind: every replay equals the eager call on the same inputs bit for bit,
+    with the flag of the form it took."""
+    L, d, Nr, Nc, K, B = 512, 256, 128, 128, 16, 16
+    N = Nr * Nc
+    cases = {}
+    for name, dist, seed in (("a", "clustered", 71), ("b", "normal", 72)):
+        w, inp_cpu = synth.make_case(L, d, Nr, Nc, K, B, "bf16", x_dist=dist, seed=seed)
+        inp = {k: v.cuda() for k, v in inp_cpu.items()}
+        br = omni.RoutedBranch(L, d, Nr, Nc, K, B, torch.bfloat16)
+        br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+        dy = synth.upstream_grad(w, seed=seed).cuda()
+        chosen = torch.empty((1,), dtype=torch.int32, device="cuda")
+        ref = omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                             chosen=chosen)
+        torch.cuda.synchronize()
+        cases[name] = (inp, br.idx.clone(), br.gate.clone(), dy, ref, int(chosen.item()))
+    assert cases["a"][5] == 1 and cases["b"][5] == 0
+    # static buffers the graph reads and writes
+    inp_a = cases["a"][0]
+    x, W, V = (inp_a[k].clone() for k in ("x", "W", "V"))
+    idx, gate, dy = cases["a"][1].clone(), cases["a"][2].clone(), cases["a"][3].clone()
+    cap = min(N, L * K)
+    f32, i32 = torch.float32, torch.int32
+    dx = torch.empty((L, d), dtype=f32, device="cuda")
+    dgate = torch.empty((L, K), dtype=f32, device="cuda")
+    uniq = torch.empty((cap,), dtype=i32, device="cuda")
+    n_uniq = torch.empty((1,), dtype=i32, device="cuda")
+    dW = torch.empty((cap, d), dtype=f32, device="cuda")
+    dV = torch.empty((cap, d), dtype=f32, device="cuda")
+    chosen = torch.empty((1,), dtype=i32, device="cuda")
+    ws = torch.empty((omni.omni_workspace_bytes(omni.OMNI_OP_EXPERT_BACKWARD_AUTO, L=L, d=d,
+                                                K=K, N=N),), dtype=torch.uint8, device="cuda")
+
+    def call():
+        omni.omni_expert_backward_auto(x, W, V, idx, gate, dy, dx, dgate, uniq, n_uniq, dW, dV,
+                                       ws, chosen=chosen)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        name = "a" if rep % 2 == 0 else "b"
+        inp, idx_c, gate_c, dy_c, ref, want = cases[name]
+        for dst, src in ((x, inp["x"]), (W, inp["W"]), (V, inp["V"]), (idx, idx_c),
+                         (gate, gate_c), (dy, dy_c)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        say(f"backward graph replay {rep} ({name})")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(chosen.item()) == want, rep
+        _assert_same_backward((dx, dgate, uniq, n_uniq, dW, dV), ref, int(ref[3].item()))
