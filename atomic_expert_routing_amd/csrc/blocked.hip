@@ -240,23 +240,36 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
   constexpr bool KEEP = E <= 16;
   int v[E], id0[KEEP ? E : 1];
   float g0[KEEP ? E : 1];
+  // row r = i / K and slot k = i % K of position i = tid*E + q: one division
+  // per thread, then one step per position (a software division per
+  // position, repeated in each pass of the scatter below, was a quarter of
+  // the kernel's code; 4 us of 485 on the skewed workload's blocked
+  // forward); kept as (r << 16) | k for the scatter (r < 2^15)
+  int rk[KEEP ? E : 1];
+  {
+    int r = (tid * E) / K, k = tid * E - r * K;
 #pragma unroll
-  for (int q = 0; q < E; ++q) {
-    const int i = tid * E + q;
-    int key = INT_MAX;
-    float g = 0.f;
-    if (i < nt) {
-      const int r = i / K;
-      const int t = slot_token(order, b * BT + r, L);
-      if (t >= 0) {
-        key = idx[(size_t)t * K + (i - r * K)];
-        if constexpr (KEEP) g = gate[(size_t)t * K + (i - r * K)];
+    for (int q = 0; q < E; ++q) {
+      const int i = tid * E + q;
+      int key = INT_MAX;
+      float g = 0.f;
+      if (i < nt) {
+        const int t = slot_token(order, b * BT + r, L);
+        if (t >= 0) {
+          key = idx[(size_t)t * K + k];
+          if constexpr (KEEP) g = gate[(size_t)t * K + k];
+        }
       }
-    }
-    v[q] = key;
-    if constexpr (KEEP) {
-      id0[q] = key;
-      g0[q] = g;
+      v[q] = key;
+      if constexpr (KEEP) {
+        id0[q] = key;
+        g0[q] = g;
+        rk[q] = (r << 16) | k;
+      }
+      if (++k == K) {
+        k = 0;
+        ++r;
+      }
     }
   }
   if constexpr (E <= 16) merge_sort<E>(keys, v, tid);
@@ -348,10 +361,10 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < E; ++q) {
-          const int i = tid * E + q, r = i / K;
+          const int r = rk[q] >> 16;
           if (id0[q] != INT_MAX && r >= r0 && r < r0 + rows) {
             stage[(r - r0) * npad + col[q]] = __float_as_uint(g0[q]);
-            if (kmap) kstage[(r - r0) * npad + col[q]] = (uint32_t)(i - r * K);
+            if (kmap) kstage[(r - r0) * npad + col[q]] = (uint32_t)(rk[q] & 0xffff);
           }
         }
         __syncthreads();
@@ -368,9 +381,9 @@ __global__ __launch_bounds__(1024) void blk_union(const int32_t* __restrict__ id
     for (int q = 0; q < E; ++q) {
       if (id0[q] == INT_MAX) continue;  // padding or an empty row
       const int c = base[q] + (keys[base[q]] < id0[q]);
-      const int i = tid * E + q, r = i / K;
+      const int r = rk[q] >> 16;
       Gb[r * npad + c] = __float_as_uint(g0[q]);
-      if (kmap) kmap[(size_t)b * BT * ucap + r * npad + c] = i - r * K;
+      if (kmap) kmap[(size_t)b * BT * ucap + r * npad + c] = rk[q] & 0xffff;
     }
   } else {
     for (int i = tid; i < nt; i += 1024) {
