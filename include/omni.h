@@ -398,7 +398,8 @@ OMNI_API omni_status omni_expert_backward_blocked(const void* x, const void* W, 
  * omni_expert_backward_auto - the gradients of omni_expert_backward, in the
  * form that suits the routing, chosen on the device per call by the rule of
  * omni_expert_forward_auto (the same sample of the tasks, so on the same idx
- * both passes of a step take the same form; the host never waits).
+ * and up to 524288 tokens both passes of a step take the same form; the host
+ * never waits).
  * Source: as omni_expert_backward; the choice answers the digest's
  * weaknesses paragraph as omni_expert_forward_auto does.
  *
