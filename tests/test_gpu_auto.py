@@ -321,3 +321,26 @@ def test_auto_backward_graph_replays_switch_form_with_the_inputs():
         torch.cuda.synchronize()
         assert int(chosen.item()) == want, rep
         _assert_same_backward((dx, dgate, uniq, n_uniq, dW, dV), ref, int(ref[3].item()))
+
+
+def test_auto_backward_above_the_blocked_token_limit_takes_per_task():
+    """Past the blocked backward's token limit the automatic backward takes the
+    per-task form even where the routing repeats its experts (here the
+    forward takes the blocked form), and equals omni_expert_backward bit for
+    bit."""
+    L, d, Nr, Nc, K, B = BLK_BWD_MAX_L + 64, 256, 8, 8, 4, 8
+    w, inp = synth.make_case(L, d, Nr, Nc, K, B, "bf16", seed=81, device="cuda")
+    say(f"auto backward past the token limit: {w.name}")
+    br = omni.RoutedBranch(L, d, Nr, Nc, K, B, torch.bfloat16)
+    br.forward(inp["x"], inp["Wr"], inp["Wc"], inp["W"], inp["V"])
+    dy = synth.upstream_grad(w, seed=81, device="cuda")
+    chosen = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    got = omni.omni_expert_backward_auto(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy,
+                                         chosen=chosen)
+    ref = omni.omni_expert_backward(inp["x"], inp["W"], inp["V"], br.idx, br.gate, dy)
+    torch.cuda.synchronize()
+    assert int(br.chosen.item()) == 1  # the forward's rule alone picks the blocked form
+    assert int(chosen.item()) == 0 == _bwd_choice(br.idx, "bf16", d, L)
+    _assert_same_backward(got, ref, int(ref[3].item()))
+    del inp, br, got, ref, dy
+    torch.cuda.empty_cache()
