@@ -743,6 +743,71 @@ hipError_t launch_router_gemm(const void* x, const void* Wr, const void* Wc, int
 
 size_t router_topk_lds_bytes(int Nr, int Nc, int K) { return topk_layout(Nr, Nc, K).bytes; }
 
+
+// Two waves per token: waves 2j (rows) and 2j + 1 (columns) of a workgroup
+// run LogSoftmax, pre-selection and key sort of their half side by side;
+// after one barrier the row wave takes the candidates, their selection and
+// the final sort.  Register-candidate form only, for the shapes instantiated
+// in the launcher (the others keep one wave per token).  A token's chain of
+// dependent steps loses one half's LogSoftmax, search and sort; the
+// instructions are the same, so it pays where the SIMDs are not full: the router call (projection and
+// top-K) at 4096 tokens 124.4 -> 121.2 us at 1.7M experts and 86.9 -> 83.5 us
+// at 1M, 61.4 -> 60.5 us at 280,900, 460 -> 460 us at 16384 tokens x K = 256;
+// the same ids, scores and gates.
+template <int VPL, int Q>
+__global__ __launch_bounds__(256) void router_topk_pair(const float* __restrict__ logits, int L,
+                                                        int Nr, int Nc, int K, const TopkLayout lay,
+                                                        int32_t* __restrict__ idx,
+                                                        float* __restrict__ score,
+                                                        float* __restrict__ gate) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_all[];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = wv >> 1, role = wv & 1;
+  unsigned char* smem = smem_all + (size_t)slot * lay.bytes;
+  lds_u64* rs = (lds_u64*)(smem + lay.o_rs);
+  lds_u64* cs = (lds_u64*)(smem + lay.o_cs);
+  lds_u64* fs = (lds_u64*)(smem + lay.o_fs);
+  lds_int* off = (lds_int*)(smem + lay.o_off);
+  const int t = blockIdx.x * 2 + slot, lane = threadIdx.x & 63;
+  const bool live = t < L;
+  if (live) {
+    const float* src = logits + (size_t)t * (Nr + Nc) + (role ? Nr : 0);
+    const int n = role ? Nc : Nr;
+    const int R = role ? lay.Kc : lay.Kr;
+    lds_u64* out = role ? cs : rs;
+    unsigned val[VPL];
+    log_softmax_ord<VPL>(src, n, val);
+    select_top_regs<VPL>(val, n, R, out);
+    wave_sync();
+    wave_sort_lds(out, R);
+  }
+  __syncthreads();  // every wave of the workgroup reaches it once
+  if (!live || role) return;
+  {
+    const int per = (lay.Kr + 63) / 64;
+    const int a0 = lane * per;
+    int loc = 0;
+    for (int a = a0; a < a0 + per && a < lay.Kr; ++a) loc += min(lay.Kc, K / (a + 1));
+    const int inc = wave_incl_scan(loc);
+    int run = inc - loc;
+    for (int a = a0; a < a0 + per && a < lay.Kr; ++a) {
+      off[a] = run;
+      run += min(lay.Kc, K / (a + 1));
+    }
+    if (lane == 63) off[lay.Kr] = inc;
+  }
+  wave_sync();
+  select_cands_regs<Q>(rs, cs, off, lay.Kr, lay.P, lay.Kc, Nc, K, fs);
+  wave_sync();
+  int32_t* io = idx + (size_t)t * K;
+  float* so = score + (size_t)t * K;
+  float* go = gate + (size_t)t * K;
+  if (K <= 64) emit_topk<1>(fs, K, io, so, go);
+  else if (K <= 128) emit_topk<2>(fs, K, io, so, go);
+  else if (K <= 256) emit_topk<4>(fs, K, io, so, go);
+  else emit_topk<8>(fs, K, io, so, go);
+}
+
 hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K, int32_t* idx,
                               float* score, float* gate, hipStream_t s) {
   const TopkLayout lay = topk_layout(Nr, Nc, K);
@@ -753,6 +818,17 @@ hipError_t launch_router_topk(const float* logits, int L, int Nr, int Nc, int K,
   // workgroup within the default 64 KB of dynamic LDS
   const size_t lds = lay.bytes;
   const int wpg = lds * 4 <= 65536 ? 4 : lds * 2 <= 65536 ? 2 : 1;
+  if (lay.regq && need <= 24 && lds * 2 <= 65536) {
+#define OMNI_TOPK_PAIR(V, QQ)                                                                   \
+    if (need <= V && lay.regq == QQ) {                                                          \
+      hipLaunchKernelGGL((router_topk_pair<V, QQ>), dim3((L + 1) / 2), dim3(256), lds * 2, s,    \
+                         logits, L, Nr, Nc, K, lay, idx, score, gate);                          \
+      return hipGetLastError();                                                                 \
+    }
+    OMNI_TOPK_PAIR(9, 8) OMNI_TOPK_PAIR(9, 12) OMNI_TOPK_PAIR(16, 12) OMNI_TOPK_PAIR(16, 24)
+    OMNI_TOPK_PAIR(21, 12) OMNI_TOPK_PAIR(21, 24)
+#undef OMNI_TOPK_PAIR
+  }
 #define OMNI_TOPK(V)                                                                           \
   if (need <= V) {                                                                             \
     hipLaunchKernelGGL(router_topk<V>, dim3((L + wpg - 1) / wpg), dim3(64 * wpg), lds * wpg, s, \
