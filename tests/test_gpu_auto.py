@@ -231,10 +231,12 @@ def test_auto_backward_one_workspace_serves_both_forms():
         _assert_same_backward(got, ref, int(ref[3].item()))
 
 
-@pytest.mark.parametrize("name", ["skewed_L16384_N1700416_d2048", synth.HEADLINE])
+@pytest.mark.parametrize("name", ["skewed_L16384_N1700416_d2048", synth.HEADLINE,
+                                  "L4096_N1048576_d1024", "L4096_N280900_d768"])
 def test_auto_backward_full_size(name):
-    """Both full-size workloads: the skewed one takes the blocked form, the
-    spread-out one the per-task form, each bit for bit."""
+    """The full-size workloads: the skewed one takes the blocked form, the
+    spread-out ones the per-task form (at d = 768 the blocked form is not
+    offered), each bit for bit."""
     w = synth.WORKLOADS[name]
     say(f"auto backward full-size {name}")
     inp = synth.make_inputs(w, seed=0, device="cuda")

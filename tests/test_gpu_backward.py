@@ -131,10 +131,12 @@ def test_backward_is_deterministic():
         assert torch.equal(a[k][:n], b[k][:n]), k
 
 
-@pytest.mark.parametrize("name", [synth.HEADLINE, "skewed_L16384_N1700416_d2048"])
+@pytest.mark.parametrize("name", [synth.HEADLINE, "skewed_L16384_N1700416_d2048",
+                                  "L4096_N1048576_d1024", "L4096_N280900_d768"])
 def test_full_size_backward_sampled(name):
-    """The 4096-token, 1.7M-expert shape and the skewed 16384-token one (K =
-    256, tasks piled onto few experts): used-expert list in full, dx and
+    """The 4096-token shapes at 1.7M, 1M and 280,900 experts and the skewed
+    16384-token one (K = 256, tasks piled onto few experts): used-expert
+    list in full, dx and
     dgate on sampled tokens, dW and dV on sampled experts (every task of
     each; fewer experts on the skewed routing, whose experts carry hundreds
     of tasks), dW_r and dW_c in full (the oracle's dense products over all
