@@ -629,11 +629,19 @@ __global__ __launch_bounds__(256) void blk_act(const uint16_t* __restrict__ x,
 // ------------------------------------------------------------------ blk_out
 // Workgroup (b, jt): y rows of block b, columns [256 jt, 256 jt + 256); 4
 // waves of 64 x 64.  A k-tile is 32 union rows: the V slice (32 x 256 bf16,
-// row-major, 16-byte chunk g of row R in slot g ^ ((R >> 3) & 3)) and the A_hi
-// and A_lo tiles (64 x 32 bf16 each) go to LDS by direct loads, through a
-// 3-stage ring.  The B operand (8 consecutive rows of one column per lane)
-// is gathered with 2-byte LDS reads, which the slot rotation spreads over
-// distinct banks.  The union ids that address a tile's V rows are read by
+// row-major, 16-byte chunk g of row R in slot g ^ (2 ((R >> 3) & 3))) and the
+// A_hi and A_lo tiles (64 x 32 bf16 each) go to LDS by direct loads, through
+// a 3-stage ring.  The B operand (8 consecutive rows of one column per lane)
+// is gathered with 2-byte LDS reads: lane group kq = lane / 16 reads rows
+// 8 kq .. 8 kq + 7, all rows fall on the same banks (512 bytes apart), and
+// the rotation puts the four groups' 16 columns in eight distinct 16-byte
+// slots.  Rotating by ((R >> 3) & 3) gave groups 0 and 1 (and 2 and 3) the
+// same two slots; the counters on the skewed workload fell from 20 M to
+// 6.7 M bank-conflict cycles per call (the rest: two lanes reading the two
+// halves of one 4-byte word), the blocked forward 490 -> 487 us.  Gathering
+// the operand with two LDS transpose reads (ds_read_b64_tr_b16) per fragment
+// instead, over a layout whose rotation also spreads the four rows a group
+// reads, was slower (487 -> 515 us) with the same y.  The union ids that address a tile's V rows are read by
 // scalar loads two tiles ahead, so the vector-load counter only ever holds
 // tile loads and the waits can leave the next tile in flight.
 constexpr int K2_COLS = BLK_D_TILE, K2_KT = 32, K2_ROWB = 2 * K2_COLS;  // 512-byte V rows
@@ -670,7 +678,8 @@ __global__ __launch_bounds__(256) void blk_out(const uint16_t* __restrict__ V,
   const int half = lane >> 5, kq = lane >> 4;
   int slotg[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) slotg[q] = (lane & 31) ^ (((8 * wave + 2 * q + half) >> 3) & 3);
+  for (int q = 0; q < 4; ++q)
+    slotg[q] = (lane & 31) ^ ((((8 * wave + 2 * q + half) >> 3) & 3) << 1);
   const int rows = SETS ? *nrows : L;
   auto item = [&](int b, int c0) {
     const int ntile = SETS ? toff[b + 1] - toff[b] : 0;
@@ -743,7 +752,7 @@ __global__ __launch_bounds__(256) void blk_out(const uint16_t* __restrict__ V,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = wave * 64 + q * 16 + (lane & 15);
-        const unsigned char* p = st + (((col >> 3) ^ kq) << 4) + ((col & 7) << 1);
+        const unsigned char* p = st + (((col >> 3) ^ (kq << 1)) << 4) + ((col & 7) << 1);
         const bf16x8 vb = vfrag(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
